@@ -1,0 +1,363 @@
+"""Pins of the CPU oracle: facts fixed by the pages and by mathematics.
+
+Each check takes the oracle module (``oracle.attention``) as its argument so
+that the mutation tests can hand it a copy with a planted mistake and show that
+some check fails.  None of these checks retypes the oracle's formulas: they use
+closed forms, invariants, hand-worked values, finite differences, and
+independent library routines (torch's scaled_dot_product_attention, logsumexp
+and autograd in float64 on the CPU).
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _dense(rng, B, nq, nk, hq, hkv, d):
+    q = rng.standard_normal((B, nq, hq, d))
+    k = rng.standard_normal((B, nk, hkv, d))
+    v = rng.standard_normal((B, nk, hkv, d))
+    return q, k, v
+
+
+# ---------------------------------------------------------------- P-1
+def check_rows_sum_to_one(A):
+    """Every row of P with a visible key sums to 1 (softmax definition)."""
+    rng = _rng(11)
+    q = rng.standard_normal((37, 16))
+    k = rng.standard_normal((53, 16))
+    for causal, window in [(False, 0), (True, 0), (True, 7), (False, 9)]:
+        p = A.probabilities(q, k, 0.7, causal, window)
+        assert np.all(p >= 0)
+        assert np.allclose(p.sum(axis=1), 1.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-2
+def check_identical_keys(A):
+    """All keys equal -> O_i is the mean of V over the keys i may see."""
+    rng = _rng(12)
+    B, n, d = 1, 24, 8
+    q = rng.standard_normal((B, n, 2, d))
+    k = np.broadcast_to(rng.standard_normal(d), (B, n, 1, d)).copy()
+    v = rng.standard_normal((B, n, 1, d))
+    o, _ = A.attn_fwd(q, k, v, 0.3, causal=False)
+    assert np.allclose(o[0, :, 0], v[0, :, 0].mean(axis=0), atol=1e-12)
+    o, _ = A.attn_fwd(q, k, v, 0.3, causal=True)
+    prefix = np.cumsum(v[0, :, 0], axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.allclose(o[0, :, 1], prefix, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-3
+def check_dominant_score(A):
+    """k_j* = alpha * q_i with alpha large -> O_i ~= V_j* within the bound."""
+    rng = _rng(13)
+    n, d = 40, 16
+    q, k, v = _dense(rng, 1, n, n, 1, 1, d)
+    i, js = 17, 5
+    k[0, js, 0] = 60.0 * q[0, i, 0]
+    o, _ = A.attn_fwd(q, k, v, 1.0, causal=False)
+    s = k[0, :, 0] @ q[0, i, 0]
+    gap = s[js] - np.max(np.delete(s, js))
+    bound = (n - 1) * math.exp(-gap) * 2 * np.abs(v).max()
+    assert gap > 30
+    assert np.max(np.abs(o[0, i, 0] - v[0, js, 0])) <= bound + 1e-12
+
+
+# ---------------------------------------------------------------- P-4
+def check_permutation_invariance(A):
+    """Permuting K and V rows together leaves non-causal O and LSE unchanged."""
+    rng = _rng(14)
+    q, k, v = _dense(rng, 2, 19, 31, 4, 2, 8)
+    perm = rng.permutation(31)
+    o1, l1 = A.attn_fwd(q, k, v, 0.4)
+    o2, l2 = A.attn_fwd(q, k[:, perm], v[:, perm], 0.4)
+    assert np.allclose(o1, o2, atol=1e-12)
+    assert np.allclose(l1, l2, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-5
+def check_lse_is_logsumexp(A):
+    """LSE = ln sum_j exp(S_ij): against long double and torch.logsumexp."""
+    rng = _rng(15)
+    q, k, v = _dense(rng, 1, 21, 29, 1, 1, 8)
+    q *= 3.0  # large scores exercise the max subtraction
+    scale = 1.3
+    _, lse = A.attn_fwd(q, k, v, scale)
+    s = scale * (q[0, :, 0] @ k[0, :, 0].T)
+    ld = np.log(np.exp(s.astype(np.longdouble)).sum(axis=1))
+    assert np.allclose(lse[0, 0], ld.astype(np.float64), atol=1e-12)
+    tl = torch.logsumexp(torch.from_numpy(s), dim=1).numpy()
+    assert np.allclose(lse[0, 0], tl, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-6
+def _visible_count(i, nq, nk, causal, window):
+    """Number of keys query i sees, by counting (closed form per case)."""
+    top = i + (nk - nq)  # last position query i may see when causal
+    hi = min(nk - 1, top) if causal else nk - 1
+    lo = max(0, top - window + 1) if window > 0 else 0
+    return max(0, hi - lo + 1)
+
+
+def check_scale_zero(A):
+    """scale = 0 -> O_i = mean of visible V, LSE_i = ln(#visible keys)."""
+    rng = _rng(16)
+    for nq, nk, causal, window in [(30, 30, True, 0), (30, 30, True, 7),
+                                   (30, 30, False, 7), (12, 30, True, 0),
+                                   (12, 30, True, 5), (30, 30, False, 0)]:
+        q, k, v = _dense(rng, 1, nq, nk, 1, 1, 4)
+        o, lse = A.attn_fwd(q, k, v, 0.0, causal=causal, window=window)
+        for i in range(nq):
+            cnt = _visible_count(i, nq, nk, causal, window)
+            top = i + nk - nq
+            hi = min(nk - 1, top) if causal else nk - 1
+            lo = max(0, top - window + 1) if window > 0 else 0
+            assert cnt == hi - lo + 1
+            assert abs(lse[0, 0, i] - math.log(cnt)) < 1e-12
+            assert np.allclose(o[0, i, 0], v[0, lo:hi + 1, 0].mean(axis=0),
+                               atol=1e-12)
+    # window closed form at the diagonal: LSE_i = ln min(i + 1, W)
+    q, k, v = _dense(rng, 1, 40, 40, 1, 1, 4)
+    _, lse = A.attn_fwd(q, k, v, 0.0, causal=True, window=9)
+    assert np.allclose(lse[0, 0], np.log(np.minimum(np.arange(40) + 1, 9)),
+                       atol=1e-12)
+    # packed batch, non-causal: LSE = ln(sequence length)
+    lengths = [5, 1, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, 2, 4))
+    k = rng.standard_normal((T, 1, 4))
+    v = rng.standard_normal((T, 1, 4))
+    o, lse = A.attn_fwd(q, k, v, 0.0, cu_seqlens=cu)
+    for s, L in enumerate(lengths):
+        a, b = cu[s], cu[s + 1]
+        assert np.allclose(lse[:, a:b], math.log(L), atol=1e-12)
+        assert np.allclose(o[a:b, 0], v[a:b, 0].mean(axis=0), atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-8
+def _torch_sdpa(q, k, v, scale, causal):
+    """torch float64 CPU SDPA on the dense layout, GQA by repeating KV heads."""
+    G = q.shape[2] // k.shape[2]
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=causal, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def check_against_torch_sdpa(A):
+    """Small shapes against torch SDPA (float64, CPU), MHA and GQA."""
+    rng = _rng(18)
+    for B, n, hq, hkv, d, causal in [(2, 33, 4, 4, 16, False),
+                                     (2, 33, 4, 4, 16, True),
+                                     (1, 50, 8, 2, 32, True),
+                                     (1, 50, 6, 1, 8, False)]:
+        q, k, v = _dense(rng, B, n, n, hq, hkv, d)
+        scale = 1.0 / math.sqrt(d)
+        o, _ = A.attn_fwd(q, k, v, scale, causal=causal)
+        assert np.allclose(o, _torch_sdpa(q, k, v, scale, causal), atol=1e-12)
+
+
+def check_brute_force_tiny(A):
+    """N=2, d=1 by hand: O_0 is the sigmoid-weighted mean of v0 and v1."""
+    q = np.array([[[[0.7]], [[-1.1]]]])          # [1, 2, 1, 1]
+    k = np.array([[[[1.5]], [[-0.4]]]])
+    v = np.array([[[[2.0]], [[-3.0]]]])
+    o, lse = A.attn_fwd(q, k, v, 1.0)
+    for i in range(2):
+        s0, s1 = q[0, i, 0, 0] * k[0, 0, 0, 0], q[0, i, 0, 0] * k[0, 1, 0, 0]
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        assert abs(o[0, i, 0, 0] - (w0 * 2.0 + (1 - w0) * -3.0)) < 1e-14
+        assert abs(lse[0, 0, i] - (s0 + math.log1p(math.exp(s1 - s0)))) < 1e-14
+
+
+def check_hand_worked_golden(A):
+    """The hand-worked example in tests/golden/hand_worked_softmax.txt."""
+    q = np.array([[1, 0], [0, 1]], float).reshape(1, 2, 1, 2)
+    k = np.array([[0, 0], [1, 0], [2, 1]], float).reshape(1, 3, 1, 2)
+    v = np.array([[7, 0], [0, 7], [1, 1]], float).reshape(1, 3, 1, 2)
+    cases = {"none": (False, 0), "causal": (True, 0), "causal_window2": (True, 2)}
+    n = 0
+    with open(os.path.join(GOLDEN, "hand_worked_softmax.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            case, row, o0, o1, lse = line.split()
+            causal, window = cases[case]
+            o, l = A.attn_fwd(q, k, v, math.log(2.0), causal, window)
+            r = int(row)
+            assert abs(o[0, r, 0, 0] - float(Fraction(o0))) < 1e-12
+            assert abs(o[0, r, 0, 1] - float(Fraction(o1))) < 1e-12
+            assert abs(l[0, 0, r] - math.log(int(lse[3:-1]))) < 1e-12
+            n += 1
+    assert n == 6
+
+
+# ---------------------------------------------------------------- P-9
+def check_gqa_is_repeated_mha(A):
+    """GQA equals MHA with each KV head repeated over its contiguous group."""
+    rng = _rng(19)
+    q, k, v = _dense(rng, 2, 17, 17, 8, 2, 8)
+    o1, l1 = A.attn_fwd(q, k, v, 0.5, causal=True)
+    kr, vr = np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2)
+    o2, l2 = A.attn_fwd(q, kr, vr, 0.5, causal=True)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    # query head 1 belongs to KV head 0: changing KV head 1 must not move it
+    k2 = k.copy()
+    k2[:, :, 1] += 5.0
+    o3, _ = A.attn_fwd(q, k2, v, 0.5, causal=True)
+    assert np.allclose(o3[:, :, :4], o1[:, :, :4], atol=1e-12)
+    # torch check of the grouping (repeat_interleave = contiguous groups)
+    assert np.allclose(o1, _torch_sdpa(q, k, v, 0.5, True), atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-10
+def check_varlen_is_concatenation(A):
+    """A packed batch equals each sequence run densely, concatenated."""
+    rng = _rng(20)
+    lengths = [7, 1, 0, 13, 4]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, 4, 8))
+    k = rng.standard_normal((T, 2, 8))
+    v = rng.standard_normal((T, 2, 8))
+    for causal, window in [(False, 0), (True, 0), (True, 3)]:
+        o, lse = A.attn_fwd(q, k, v, 0.6, causal, window, cu_seqlens=cu)
+        for s, L in enumerate(lengths):
+            a, b = cu[s], cu[s + 1]
+            if L == 0:
+                continue
+            od, ld = A.attn_fwd(q[None, a:b], k[None, a:b], v[None, a:b],
+                                0.6, causal, window)
+            assert np.allclose(o[a:b], od[0], atol=1e-12)
+            assert np.allclose(lse[:, a:b], ld[0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-11
+def check_key_translation(A):
+    """K += 1 c^T leaves O unchanged and shifts LSE_i by scale * q_i . c."""
+    rng = _rng(21)
+    q, k, v = _dense(rng, 1, 23, 23, 2, 1, 8)
+    c = rng.standard_normal(8)
+    for causal in (False, True):
+        o1, l1 = A.attn_fwd(q, k, v, 0.45, causal)
+        o2, l2 = A.attn_fwd(q, k + c, v, 0.45, causal)
+        assert np.allclose(o1, o2, atol=1e-11)
+        shift = 0.45 * np.einsum("bnhd,d->bhn", q, c)
+        assert np.allclose(l2, l1 + shift, atol=1e-11)
+
+
+# ---------------------------------------------------------------- P-12
+def _loss(A, q, k, v, do, scale, causal, window):
+    o, _ = A.attn_fwd(q, k, v, scale, causal, window)
+    return float((o * do).sum())
+
+
+def check_backward_finite_differences(A):
+    """Central finite differences of sum(O * dO), fp64, tiny shapes."""
+    rng = _rng(22)
+    for causal, window in [(False, 0), (True, 0), (True, 3)]:
+        q, k, v = _dense(rng, 1, 6, 6, 2, 1, 3)
+        do = rng.standard_normal(q.shape)
+        dq, dk, dv = A.attn_bwd(q, k, v, do, 0.8, causal, window)
+        h = 1e-6
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                x[idx] += h
+                fp = _loss(A, q, k, v, do, 0.8, causal, window)
+                x[idx] -= 2 * h
+                fm = _loss(A, q, k, v, do, 0.8, causal, window)
+                x[idx] += h
+                num[idx] = (fp - fm) / (2 * h)
+            err = np.abs(num - g).max() / max(np.abs(num).max(), 1e-30)
+            assert err < 1e-6, err
+
+
+def check_backward_autograd(A):
+    """Against torch autograd through float64 SDPA (GQA by repeat)."""
+    rng = _rng(23)
+    for causal in (False, True):
+        q, k, v = _dense(rng, 2, 20, 20, 4, 2, 8)
+        do = rng.standard_normal(q.shape)
+        dq, dk, dv = A.attn_bwd(q, k, v, do, 0.35, causal)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True)
+                      for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq.permute(0, 2, 1, 3),
+            tk.permute(0, 2, 1, 3).repeat_interleave(2, dim=1),
+            tv.permute(0, 2, 1, 3).repeat_interleave(2, dim=1),
+            is_causal=causal, scale=0.35).permute(0, 2, 1, 3)
+        (o * torch.from_numpy(do)).sum().backward()
+        assert np.allclose(dq, tq.grad.numpy(), atol=1e-11)
+        assert np.allclose(dk, tk.grad.numpy(), atol=1e-11)
+        assert np.allclose(dv, tv.grad.numpy(), atol=1e-11)
+
+
+def check_backward_invariants(A):
+    """sum_j dK_j = 0 and sum_j dV_j = sum of dO over the group's queries."""
+    rng = _rng(24)
+    q, k, v = _dense(rng, 1, 15, 15, 4, 2, 8)
+    do = rng.standard_normal(q.shape)
+    for causal, window in [(False, 0), (True, 0), (True, 4)]:
+        _, dk, dv = A.attn_bwd(q, k, v, do, 0.5, causal, window)
+        assert np.allclose(dk.sum(axis=1), 0.0, atol=1e-11)
+        dsum = do.reshape(1, 15, 2, 2, 8).sum(axis=(1, 3))
+        assert np.allclose(dv.sum(axis=1), dsum, atol=1e-11)
+
+
+# ---------------------------------------------------------------- P-13
+def check_causal_row_zero(A):
+    """Causal row 0 sees only key 0: O_0 = V_0, LSE_0 = scale q0.k0, dQ_0 = 0."""
+    rng = _rng(25)
+    q, k, v = _dense(rng, 1, 9, 9, 2, 1, 8)
+    do = rng.standard_normal(q.shape)
+    o, lse = A.attn_fwd(q, k, v, 0.3, causal=True)
+    dq, _, _ = A.attn_bwd(q, k, v, do, 0.3, causal=True)
+    for h in range(2):
+        assert np.array_equal(o[0, 0, h], v[0, 0, 0])
+        assert abs(lse[0, h, 0] - 0.3 * q[0, 0, h] @ k[0, 0, 0]) < 1e-14
+        assert np.all(dq[0, 0, h] == 0.0)
+
+
+# ------------------------------------------------- causal alignment (C-6)
+def check_chunked_prefill_alignment(A):
+    """Nq < Nk causal = the last Nq rows of the full causal problem."""
+    rng = _rng(26)
+    q, k, v = _dense(rng, 1, 24, 24, 2, 2, 8)
+    for window in (0, 5):
+        of, lf = A.attn_fwd(q, k, v, 0.5, True, window)
+        oc, lc = A.attn_fwd(q[:, 16:], k, v, 0.5, True, window)
+        assert np.allclose(oc, of[:, 16:], atol=1e-12)
+        assert np.allclose(lc, lf[:, :, 16:], atol=1e-12)
+
+
+def check_empty_rows(A):
+    """A query with no visible key gives O = 0 and LSE = -inf (no NaN)."""
+    rng = _rng(27)
+    q, k, v = _dense(rng, 1, 4, 2, 1, 1, 4)  # Nq > Nk: rows 0,1 see nothing
+    o, lse = A.attn_fwd(q, k, v, 0.5, causal=True)
+    assert np.all(o[0, :2] == 0) and np.all(np.isneginf(lse[0, 0, :2]))
+    assert np.all(np.isfinite(o[0, 2:])) and np.all(np.isfinite(lse[0, 0, 2:]))
+
+
+ALL_FORWARD = [check_rows_sum_to_one, check_identical_keys, check_dominant_score,
+               check_permutation_invariance, check_lse_is_logsumexp,
+               check_scale_zero, check_against_torch_sdpa, check_brute_force_tiny,
+               check_hand_worked_golden, check_gqa_is_repeated_mha,
+               check_varlen_is_concatenation, check_key_translation,
+               check_causal_row_zero, check_chunked_prefill_alignment,
+               check_empty_rows]
+ALL_BACKWARD = [check_backward_finite_differences, check_backward_autograd,
+                check_backward_invariants]

@@ -1,0 +1,220 @@
+"""CPU tests of the oracle against its pins (no GPU, no HIP library)."""
+
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as A
+from tests import oracle_pins as pins
+import workloads
+
+
+@pytest.mark.parametrize("check", pins.ALL_FORWARD + pins.ALL_BACKWARD,
+                         ids=lambda f: f.__name__)
+def test_pin(check):
+    check(A)
+
+
+# ----------------------------------------------------------- mutation tests
+# Plant a plausible mistake in a copy of the oracle and require that at least
+# one pin catches it.  The copy is a fresh module object whose globals are a
+# shallow copy of the oracle module's, so the real oracle is never touched.
+
+def _mutant(**overrides):
+    m = types.ModuleType("oracle_mutant")
+    m.__dict__.update({k: v for k, v in A.__dict__.items()
+                       if not k.startswith("__")})
+    # functions look up globals in their defining module: rebind them
+    for name, obj in list(m.__dict__.items()):
+        if isinstance(obj, types.FunctionType) and obj.__module__ == A.__name__:
+            m.__dict__[name] = types.FunctionType(obj.__code__, m.__dict__, name,
+                                                  obj.__defaults__, obj.__closure__)
+    m.__dict__.update(overrides)
+    return m
+
+
+def _caught(mutant, checks):
+    for check in checks:
+        try:
+            with np.errstate(all="ignore"):
+                check(mutant)
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            return True
+    return False
+
+
+def _bad_window_mask(nq, nk, causal, window):
+    i = np.arange(nq)[:, None] + (nk - nq)
+    j = np.arange(nk)[None, :]
+    ok = np.ones((nq, nk), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window > 0:
+        ok &= (i - j) <= window  # admits W + 1 keys
+    return ok
+
+
+def _top_left_causal(nq, nk, causal, window):
+    i = np.arange(nq)[:, None]
+    j = np.arange(nk)[None, :]
+    ok = np.ones((nq, nk), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window > 0:
+        ok &= (i - j) < window
+    return ok
+
+
+def _no_max_softmax(s):
+    e = np.exp(s)
+    l = e.sum(axis=1)
+    return e / l[:, None], np.log(l)
+
+
+def _lse_without_max(s):
+    p, lse = A._softmax_rows(s)
+    m = s.max(axis=1)
+    return p, lse - np.where(np.isfinite(m), m, 0.0)
+
+
+def _head_fwd_no_scale(q, k, v, scale, ok):
+    s = np.where(ok, q @ k.T, -np.inf)
+    p, lse = A._softmax_rows(s)
+    return p @ v, lse, p
+
+
+def _head_bwd_missing_D(q, k, v, do, scale, ok):
+    o, _, p = A._head_fwd(q, k, v, scale, ok)
+    ds = p * (do @ v.T)
+    return scale * (ds @ k), scale * (ds.T @ q), p.T @ do
+
+
+def _head_bwd_unscaled_dk(q, k, v, do, scale, ok):
+    dq, dk, dv = A._head_bwd(q, k, v, do, scale, ok)
+    return dq, dk / scale, dv
+
+
+def _head_bwd_transposed_dv(q, k, v, do, scale, ok):
+    dq, dk, _ = A._head_bwd(q, k, v, do, scale, ok)
+    _, _, p = A._head_fwd(q, k, v, scale, ok)
+    return dq, dk, p @ do  # P instead of P^T (the pins use square shapes)
+
+
+MUTATIONS = {
+    "gqa_strided_groups": dict(kv_head_of=lambda h, hq, hkv: h % hkv),
+    "window_off_by_one": dict(allowed_mask=_bad_window_mask),
+    "causal_top_left": dict(allowed_mask=_top_left_causal),
+    "softmax_without_max": dict(_softmax_rows=_no_max_softmax),
+    "lse_missing_max": dict(_softmax_rows=_lse_without_max),
+    "scale_dropped": dict(_head_fwd=_head_fwd_no_scale),
+    "bwd_missing_D": dict(_head_bwd=_head_bwd_missing_D),
+    "bwd_dk_unscaled": dict(_head_bwd=_head_bwd_unscaled_dk),
+    "bwd_dv_transposed": dict(_head_bwd=_head_bwd_transposed_dv),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    mutant = _mutant(**MUTATIONS[name])
+    assert _caught(mutant, pins.ALL_FORWARD + pins.ALL_BACKWARD), name
+
+
+def test_mutant_harness_is_faithful():
+    """An unmutated copy passes every pin (so catches above are real)."""
+    assert not _caught(_mutant(), pins.ALL_FORWARD + pins.ALL_BACKWARD)
+
+
+# ------------------------------------------------------------------- P-7
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 11),
+                                           (False, 6)])
+def test_online_recurrence_matches_definition(causal, window):
+    """The pages' running (m, l, O) recurrence gives the exact result."""
+    rng = np.random.default_rng(30)
+    nq, nk, d = 45, 77, 16
+    q = rng.standard_normal((nq, d)) * 2
+    k = rng.standard_normal((nk, d))
+    v = rng.standard_normal((nk, d))
+    o_ref, l_ref = A.attn_fwd(q[None, :, None], k[None, :, None],
+                              v[None, :, None], 0.6, causal, window)
+    for trial in range(5):
+        sizes = []
+        while sum(sizes) < nk:
+            sizes.append(int(rng.integers(1, 20)))
+        o, lse = oracle.online_attention(q, k, v, 0.6, sizes, causal, window)
+        assert np.allclose(o, o_ref[0, :, 0], atol=1e-12, rtol=0)
+        assert np.allclose(lse, l_ref[0, 0], atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------- sampled oracle paths
+def test_rows_path_matches_full():
+    rng = np.random.default_rng(31)
+    q, k, v = (rng.standard_normal((1, 70, 4, 8)) for _ in range(3))
+    k, v = k[:, :, :2], v[:, :, :2]
+    for causal, window in [(True, 0), (True, 9), (False, 0)]:
+        o, lse = A.attn_fwd(q, k, v, 0.4, causal, window)
+        rows = np.array([0, 3, 31, 69])
+        for h in range(4):
+            g = A.kv_head_of(h, 4, 2)
+            orow, lrow = A.attn_fwd_rows(q[0, :, h], k[0, :, g], v[0, :, g], rows,
+                                         0.4, causal, window)
+            assert np.allclose(orow, o[0, rows, h], atol=1e-13)
+            assert np.allclose(lrow, lse[0, h, rows], atol=1e-13)
+
+
+def test_sampled_backward_matches_full():
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((2, 40, 4, 8))
+    k = rng.standard_normal((2, 40, 2, 8))
+    v = rng.standard_normal((2, 40, 2, 8))
+    do = rng.standard_normal(q.shape)
+    for causal, window in [(True, 0), (False, 0), (True, 7)]:
+        dq, dk, dv = A.attn_bwd(q, k, v, do, 0.3, causal, window)
+        qr, kr = np.array([0, 5, 39]), np.array([0, 17, 39])
+        for b in range(2):
+            for g in range(2):
+                sq, sk, sv = A.attn_bwd_sampled(q, k, v, do, 0.3, causal, window,
+                                                b, g, qr, kr, chunk=13)
+                assert np.allclose(sq, dq[b][qr][:, 2 * g:2 * g + 2], atol=1e-12)
+                assert np.allclose(sk, dk[b, kr, g], atol=1e-12)
+                assert np.allclose(sv, dv[b, kr, g], atol=1e-12)
+
+
+def test_nan_poisoning_pattern():
+    """NaN in one query row poisons that row only; NaN in a key row poisons
+    the rows that see it (non-causal: all; causal: rows at or after it)."""
+    rng = np.random.default_rng(33)
+    q, k, v = (rng.standard_normal((1, 12, 1, 4)) for _ in range(3))
+    q2 = q.copy()
+    q2[0, 5, 0, 0] = np.nan
+    o, lse = A.attn_fwd(q2, k, v, 0.5)
+    assert np.all(np.isnan(o[0, 5])) and np.isnan(lse[0, 0, 5])
+    assert np.all(np.isfinite(np.delete(o[0], 5, axis=0)))
+    k2 = k.copy()
+    k2[0, 7, 0, 1] = np.nan
+    o, _ = A.attn_fwd(q, k2, v, 0.5, causal=True)
+    assert np.all(np.isfinite(o[0, :7])) and np.all(np.isnan(o[0, 7:]))
+
+
+# ---------------------------------------------------------------- inputs
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal(100000, dtype=np.float32) * 10
+    x[:4] = [np.inf, -np.inf, 0.0, -0.0]
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(workloads.round_bf16(x), ref)
+
+
+def test_workload_shapes_and_determinism():
+    a = workloads.make_inputs("varlen_window")
+    b = workloads.make_inputs("varlen_window")
+    assert np.array_equal(a["cu_seqlens"], b["cu_seqlens"])
+    assert a["q"].shape == (a["T"], 32, 128) and a["k"].shape == (a["T"], 8, 128)
+    L = np.diff(a["cu_seqlens"])
+    assert len(L) == 16 and L.min() >= 256 and L.max() <= 8192
+    s = workloads.make_inputs({"B": 1, "Hq": 4, "Hkv": 2, "N": 64, "d": 64,
+                               "seed": 7, "bwd": True})
+    assert s["q"].shape == (1, 64, 4, 64) and s["do"].shape == (1, 64, 4, 64)
+    assert np.array_equal(workloads.round_bf16(s["q"]), s["q"])

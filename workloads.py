@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module only draws and rounds data; it holds none of the attention
+arithmetic, and neither the CPU oracle nor the HIP library depends on it.
+
+Every tensor is drawn i.i.d. N(0, 1) in float32 with numpy's PCG64
+(``numpy.random.default_rng(seed)``), in token-major layout with the head
+dimension innermost, then (for bf16 workloads) rounded to bfloat16 by
+round-to-nearest-even.  The arrays returned are float32 holding exactly the
+bf16 values, so the GPU (after an exact cast to bf16) and the oracle (after an
+exact cast to fp64) see identical numbers.
+
+Draw order per workload: sequence lengths (packed batches only), then Q, K, V,
+then dO (workloads with a backward pass).
+"""
+
+import math
+
+import numpy as np
+
+# The five workloads of the hot path, named by what they are.
+#   seed: the rng seed (one per workload; a second seed = seed + 100 is used
+#         by tests that want fresh data).
+WORKLOADS = {
+    # single-head fp32, B=1 H=1 N=128 d=64, non-causal
+    "single_head_f32": dict(B=1, Hq=1, Hkv=1, N=128, d=64, dtype="f32",
+                            causal=False, window=0, seed=1),
+    # multi-head bf16 d=64, B=4 H=16 N=2048, non-causal and causal
+    "mha_d64": dict(B=4, Hq=16, Hkv=16, N=2048, d=64, dtype="bf16",
+                    causal=False, window=0, seed=2),
+    "mha_d64_causal": dict(B=4, Hq=16, Hkv=16, N=2048, d=64, dtype="bf16",
+                           causal=True, window=0, seed=2),
+    # Llama-style GQA causal prefill, B=1 Hq=32 Hkv=8 N=8192 d=128
+    "gqa_causal_prefill": dict(B=1, Hq=32, Hkv=8, N=8192, d=128, dtype="bf16",
+                               causal=True, window=0, seed=3),
+    # packed batch of 16 sequences, lengths U{256..8192}, causal + window 4096
+    "varlen_window": dict(nseq=16, Lmin=256, Lmax=8192, Hq=32, Hkv=8, d=128,
+                          dtype="bf16", causal=True, window=4096, seed=4),
+    # long causal forward + recomputation backward, B=2 H=16 N=16384 d=128
+    "long_fwd_bwd": dict(B=2, Hq=16, Hkv=16, N=16384, d=128, dtype="bf16",
+                         causal=True, window=0, seed=5, bwd=True),
+}
+
+
+def round_bf16(x):
+    """Round float32 values to the nearest bfloat16 (ties to even), as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32)
+    return np.where(nan, np.float32(np.nan), out)
+
+
+def _draw(rng, shape, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return round_bf16(x) if dtype == "bf16" else x
+
+
+def make_inputs(spec, seed=None, with_grad=None):
+    """Draw one workload's inputs.
+
+    spec: a WORKLOADS name or a dict with the same keys.  Dense specs need
+    B, Hq, Hkv, N (or Nq and Nk), d; packed specs need nseq, Lmin, Lmax (or
+    an explicit ``lengths`` list), Hq, Hkv, d.
+
+    Returns a dict with q, k, v (and do when the workload has a backward),
+    cu_seqlens (int32, or None), the shape fields, the scale 1/sqrt(d), and
+    the mask flags.
+    """
+    if isinstance(spec, str):
+        spec = WORKLOADS[spec]
+    spec = dict(spec)
+    seed = spec.get("seed", 0) if seed is None else seed
+    with_grad = spec.get("bwd", False) if with_grad is None else with_grad
+    dtype = spec.get("dtype", "bf16")
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = spec["Hq"], spec["Hkv"], spec["d"]
+    out = dict(spec)
+    if "nseq" in spec or "lengths" in spec:
+        if "lengths" in spec:
+            lengths = np.asarray(spec["lengths"], dtype=np.int64)
+        else:
+            lengths = rng.integers(spec["Lmin"], spec["Lmax"] + 1,
+                                   size=spec["nseq"])
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        T = int(cu[-1])
+        qs, ks = (T, hq, d), (T, hkv, d)
+        out.update(B=len(lengths), Nq=int(max(lengths.max(), 1)) if len(lengths) else 1,
+                   Nk=int(max(lengths.max(), 1)) if len(lengths) else 1,
+                   T=T, lengths=lengths, cu_seqlens=cu)
+    else:
+        B = spec["B"]
+        nq = spec.get("Nq", spec.get("N"))
+        nk = spec.get("Nk", spec.get("N"))
+        qs, ks = (B, nq, hq, d), (B, nk, hkv, d)
+        out.update(Nq=nq, Nk=nk, cu_seqlens=None)
+    out["q"] = _draw(rng, qs, dtype)
+    out["k"] = _draw(rng, ks, dtype)
+    out["v"] = _draw(rng, ks, dtype)
+    if with_grad:
+        out["do"] = _draw(rng, qs, dtype)
+    out["scale"] = spec.get("scale", 1.0 / math.sqrt(d))
+    out.setdefault("causal", False)
+    out.setdefault("window", 0)
+    out["dtype"] = dtype
+    return out
