@@ -1,0 +1,290 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--all] [--copy-calibration]
+
+One step = one fa_fwd call over the whole workload: work partition, Q/K/V
+tile loads, QK^T, masking, online softmax, PV and the epilogue all run in the
+one forward kernel.  The default workload is the GQA causal prefill (B=1,
+Hq=32, Hkv=8, N=8192, d=128, bf16).  Inputs are seeded synthetic N(0,1) values
+already resident in HBM when the timed region starts.  Timing uses HIP events
+recorded on the stream the kernel runs on (torch's current stream).
+
+Prints one JSON line with the throughput in attention TFLOP/s (4 B Hq Nq Nk d,
+halved for causal), the roofline position of the forward kernel, and the CPU
+oracle timed on this host on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention TFLOP/s + % of bf16 MFMA peak, causal fwd N=8192 d=128 GQA"
+FWD_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h", "fa_params.h"]
+
+
+def attention_flops(inp):
+    """Algorithmic forward FLOPs: 4 B Hq Nq Nk d, halved for causal; for
+    windowed packed batches 4 Hq d times the exact number of visible pairs."""
+    d, hq = inp["d"], inp["Hq"]
+    if inp.get("cu_seqlens") is None and inp.get("window", 0) <= 0:
+        f = 4.0 * inp["B"] * hq * inp["Nq"] * inp["Nk"] * d
+        return f / 2 if inp["causal"] else f
+    lengths = (np.diff(inp["cu_seqlens"]) if inp.get("cu_seqlens") is not None
+               else [inp["Nq"]] * inp["B"])
+    W = inp.get("window", 0)
+    pairs = 0
+    for L in lengths:
+        L = int(L)
+        if inp["causal"]:
+            pairs += L * (L + 1) // 2 if (W <= 0 or L <= W) else W * (W + 1) // 2 + (L - W) * W
+        else:
+            pairs += L * L if W <= 0 else sum(L - max(0, i - W + 1) for i in range(L))
+    return 4.0 * hq * d * pairs
+
+
+def algorithmic_bytes(inp):
+    """Bytes the forward must move: Q, K, V read once, O and LSE written once."""
+    e = 2 if inp["dtype"] == "bf16" else 4
+    nq = inp["q"].size
+    nk = inp["k"].size
+    rows = inp["q"].shape[0] * (inp["q"].shape[1] if inp["q"].ndim == 4 else 1)
+    return e * (2 * nq + 2 * nk) + 4 * rows * inp["Hq"]
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_28_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current forward-kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_bf16_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(FWD_SOURCES):
+        return None
+    return float(m_bytes.group(1))
+
+
+def blas_threads():
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        n = [x["num_threads"] for x in info if x.get("user_api") == "blas"]
+        return int(n[0]) if n else 1
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The fp64 oracle on whole heads of the same workload, until the budget
+    is spent; rate in the same algorithmic FLOP units as the GPU figure."""
+    import oracle
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, N, hq, d = q.shape
+    hkv = k.shape[2]
+    per_head = attention_flops(dict(inp, B=1, Hq=1))
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(B):
+        for h in range(hq):
+            g = oracle.kv_head_of(h, hq, hkv)
+            oracle.attn_fwd_rows(q[b, :, h], k[b, :, g], v[b, :, g], np.arange(N),
+                                 inp["scale"], inp["causal"], inp["window"])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    return {"value": per_head * done / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {B * hq} (batch, query head) pairs, all {N} rows each, "
+                      f"fp64 NumPy, {dt:.1f} s"}
+
+
+def device_inputs(inp):
+    import torch
+    dt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    mk = lambda x: torch.from_numpy(x).to(dt).cuda()
+    out = {n: mk(inp[n]) for n in ("q", "k", "v")}
+    cu = inp.get("cu_seqlens")
+    out["cu"] = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    return out
+
+
+def time_forward(inp, dev, steps, warmup):
+    import torch
+    import exact_io_aware_28_amd as fa
+    fn = fa.fa_fwd if inp["dtype"] == "bf16" else fa.fa_fwd_f32
+    kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"],
+              cu_seqlens=dev["cu"], max_seqlen=inp["Nq"] if dev["cu"] is not None else None)
+    o, lse = fn(dev["q"], dev["k"], dev["v"], **kw)
+    for _ in range(warmup):
+        fn(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step (= per launch)
+
+
+def time_backward(inp, dev, steps, warmup):
+    import torch
+    import exact_io_aware_28_amd as fa
+    kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"],
+              cu_seqlens=dev["cu"], max_seqlen=inp["Nq"] if dev["cu"] is not None else None)
+    o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], **kw)
+    do = torch.from_numpy(inp["do"]).to(torch.bfloat16).cuda()
+    dq, dk, dv = fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, do, lse, **kw)
+    ws = torch.empty(fa.fa_bwd_workspace_size(inp["B"] * inp["Nq"], inp["Hq"], inp["d"]),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "reps": reps}))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_causal_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--all", action="store_true",
+                    help="also time every other workload and the backward (extra lines)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {a.gpus}); "
+              "the attention path shards over (sequence, KV-head) units with no "
+              "communication, so a multi-GPU run is one independent run per GPU.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    import exact_io_aware_28_amd as fa
+    fa.lib()  # fails loudly when the HIP library is missing
+
+    if a.copy_calibration:
+        copy_calibration()
+        return 0
+
+    inp = workloads.make_inputs(a.workload)
+    dev = device_inputs(inp)
+    ms = time_forward(inp, dev, a.steps, a.warmup)
+    flops = attention_flops(inp)
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(a.workload)
+    cfg = {"workload": a.workload}
+    for key in ("B", "Hq", "Hkv", "N", "d", "causal", "window", "nseq", "T"):
+        if key in inp and key not in ("q", "k", "v"):
+            cfg[key] = int(inp[key]) if not isinstance(inp[key], bool) else inp[key]
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp["dtype"],
+        "data": "synthetic",
+        "config": cfg,
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "hbm_gbs_algorithmic": round(algorithmic_bytes(inp) / (ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_bf16_kernel",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": algorithmic_bytes(inp),
+        },
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, a.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+    if a.all:
+        for name in workloads.WORKLOADS:
+            if name == a.workload:
+                continue
+            wi = workloads.make_inputs(name)
+            wd = device_inputs(wi)
+            wms = time_forward(wi, wd, max(a.steps, 10), a.warmup)
+            extra = {"workload": name, "direction": "fwd", "ms": round(wms, 4),
+                     "TFLOP/s": round(attention_flops(wi) / (wms * 1e-3) / 1e12, 2)}
+            print(json.dumps(extra), flush=True)
+            if wi.get("bwd"):
+                bms = time_backward(wi, wd, 5, 1)
+                print(json.dumps({"workload": name, "direction": "bwd", "ms": round(bms, 4),
+                                  "TFLOP/s": round(2.5 * attention_flops(wi) / (bms * 1e-3) / 1e12, 2)}),
+                      flush=True)
+            del wd
+            torch.cuda.empty_cache()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

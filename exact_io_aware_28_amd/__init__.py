@@ -1,0 +1,169 @@
+"""Python binding of libfa_mi355x (exact IO-aware attention for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the shared library.  PyTorch supplies device memory and the
+stream; nothing here computes attention.  If the library is not built the
+import still succeeds but every call raises.
+
+Functions mirror the C ABI in include/fa_mi355x.h:
+    fa_fwd(q, k, v, scale, causal, window, cu_seqlens, max_seqlen) -> (o, lse)
+    fa_fwd_f32(...)  same, fp32 tensors
+    fa_bwd(q, k, v, o, dout, lse, scale, ...) -> (dq, dk, dv)
+    fa_bwd_workspace_size(T_q, Hq, d) -> int
+    fa_status_string(status) -> str
+"""
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {fa_status_string(status)} ({status})")
+
+
+def lib():
+    """The loaded ctypes library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m exact_io_aware_28_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        fwd_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, vp]
+        L.fa_fwd.argtypes = fwd_args
+        L.fa_fwd.restype = i
+        L.fa_fwd_f32.argtypes = fwd_args
+        L.fa_fwd_f32.restype = i
+        L.fa_bwd_workspace_size.argtypes = [i, i, i]
+        L.fa_bwd_workspace_size.restype = ctypes.c_size_t
+        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                             i, i, i, i, i, i, f, i, i, vp, vp]
+        L.fa_bwd.restype = i
+        L.fa_status_string.argtypes = [i]
+        L.fa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def fa_status_string(status):
+    return lib().fa_status_string(int(status)).decode()
+
+
+def fa_bwd_workspace_size(T_q, Hq, d):
+    return int(lib().fa_bwd_workspace_size(int(T_q), int(Hq), int(d)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _geometry(q, k, cu_seqlens, max_seqlen):
+    """(B, Hq, Hkv, Nq, Nk, d) from the tensor shapes (layouts of the ABI)."""
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("dense q/k/v must be [B, N, H, d]")
+        B, nq, hq, d = q.shape
+        nk, hkv = k.shape[1], k.shape[2]
+        return B, hq, hkv, nq, nk, d
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed q/k/v must be [T, H, d]")
+    if max_seqlen is None:
+        raise ValueError("packed batches need max_seqlen")
+    B = cu_seqlens.numel() - 1
+    return B, q.shape[1], k.shape[1], int(max_seqlen), int(max_seqlen), q.shape[2]
+
+
+def _check(tensors, dtype):
+    for name, t in tensors.items():
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _lse_shape(q, B, hq, nq, cu_seqlens):
+    return (B, hq, nq) if cu_seqlens is None else (hq, q.shape[0])
+
+
+def _fwd(fn, dtype, q, k, v, scale, causal, window, cu_seqlens, max_seqlen, out,
+         lse, stream):
+    import torch
+    _check({"q": q, "k": k, "v": v}, dtype)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(_lse_shape(q, B, hq, nq, cu_seqlens), dtype=torch.float32,
+                          device=q.device)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv, nq, nk, d,
+            float(scale), int(bool(causal)), int(window), _ptr(cu_seqlens),
+            _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, fn.__name__)
+    return out, lse
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, window=0, cu_seqlens=None,
+           max_seqlen=None, out=None, lse=None, stream=None):
+    """bf16 forward; returns (o bf16, lse fp32).  See include/fa_mi355x.h."""
+    import torch
+    return _fwd(lib().fa_fwd, torch.bfloat16, q, k, v, scale, causal, window,
+                cu_seqlens, max_seqlen, out, lse, stream)
+
+
+def fa_fwd_f32(q, k, v, scale=None, causal=False, window=0, cu_seqlens=None,
+               max_seqlen=None, out=None, lse=None, stream=None):
+    """fp32 forward; returns (o fp32, lse fp32)."""
+    import torch
+    return _fwd(lib().fa_fwd_f32, torch.float32, q, k, v, scale, causal, window,
+                cu_seqlens, max_seqlen, out, lse, stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
+           cu_seqlens=None, max_seqlen=None, dq=None, dk=None, dv=None,
+           workspace=None, stream=None):
+    """bf16 backward by recomputation; returns (dq, dk, dv)."""
+    import torch
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, torch.bfloat16)
+    _check({"lse": lse}, torch.float32)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(),
+                      B, hq, hkv, nq, nk, d, float(scale), int(bool(causal)),
+                      int(window), _ptr(cu_seqlens), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

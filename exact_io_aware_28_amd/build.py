@@ -1,0 +1,81 @@
+"""Build libfa_mi355x.so for gfx950 in-tree with hipcc.
+
+    python -m exact_io_aware_28_amd.build [--jobs N] [--debug-sync]
+
+Each .hip source under csrc/ is compiled to an object in _build/ (in
+parallel), then linked into exact_io_aware_28_amd/libfa_mi355x.so.  Every
+call recompiles everything.
+"""
+
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libfa_mi355x.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+CFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # no packed fp32 instructions in generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+    "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _compile(src, extra):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in l)
+    return src, obj, r.returncode, msgs
+
+
+def build(jobs=None, extra=(), verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4)
+    objs = []
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for src, obj, rc, msgs in ex.map(lambda s: _compile(s, list(extra)), srcs):
+            if msgs.strip() and (rc != 0 or verbose):
+                print(msgs, file=sys.stderr)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {src}")
+            objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        print(r.stdout + r.stderr, file=sys.stderr)
+        raise RuntimeError("link failed")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--resource-usage", action="store_true",
+                    help="print per-kernel register/LDS usage")
+    a = ap.parse_args(argv)
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if a.resource_usage else []
+    print(build(a.jobs, extra, a.verbose or a.resource_usage))
+
+
+if __name__ == "__main__":
+    main()

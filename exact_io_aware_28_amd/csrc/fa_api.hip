@@ -1,0 +1,159 @@
+// C ABI of libfa_mi355x (declared in include/fa_mi355x.h): argument
+// validation, then dispatch to the kernel launchers.
+//
+// Validation touches no HIP API, so a rejected call enqueues nothing and the
+// checks can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include <climits>
+
+#include "fa_mi355x.h"
+#include "fa_params.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by every entry point.  `elem_align` is the required pointer
+// alignment of the q/k/v/o-like tensors (16 bytes: the kernels move them in
+// 128-bit pieces).
+int check_common(const void* const* tensors, int ntensors, const float* const* stats,
+                 int nstats, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, int window, const int32_t* cu_seqlens,
+                 int qtile_rows) {
+  for (int i = 0; i < ntensors; ++i)
+    if (!tensors[i] || !aligned(tensors[i], 16)) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < nstats; ++i)
+    if (!stats[i] || !aligned(stats[i], 4)) return FA_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (window < 0) return FA_ERR_INVALID_ARG;
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (cu_seqlens && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  // element offsets are 64-bit; the launch grid must fit 32 bits
+  const int64_t tiles = (int64_t)B * Hq * ((Nq + qtile_rows - 1) / qtile_rows);
+  if (tiles > (int64_t)UINT32_MAX / 2) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Nq * Hq > (int64_t)INT32_MAX * 64) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                         int causal, int window, const int32_t* cu) {
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_seqlens = cu;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.group = Hq / Hkv;
+  p.causal = causal;
+  p.window = window;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.num_qtiles = 0;  // set by the launcher from its tile height
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+           int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+           const int32_t* cu_seqlens, void* stream) {
+  const void* t[] = {q, k, v, o};
+  const float* s[] = {lse};
+  int st = check_common(t, 4, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                        cu_seqlens, 64);
+  if (st != FA_OK) return st;
+  fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                               window, cu_seqlens);
+  return fa::launch_fwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+               int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+               const int32_t* cu_seqlens, void* stream) {
+  const void* t[] = {q, k, v, o};
+  const float* s[] = {lse};
+  int st = check_common(t, 4, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                        cu_seqlens, 64);
+  if (st != FA_OK) return st;
+  fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                               window, cu_seqlens);
+  return fa::launch_fwd_f32(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int T_q, int Hq, int d) {
+  (void)d;
+  if (T_q < 1 || Hq < 1) return 0;
+  // D_i per (head, query row), fp32, rounded up to 256 bytes
+  const size_t bytes = (size_t)T_q * (size_t)Hq * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, int window, const int32_t* cu_seqlens, void* stream) {
+  const void* t[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+  const float* s[] = {lse};
+  int st = check_common(t, 9, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                        cu_seqlens, 64);
+  if (st != FA_OK) return st;
+  // packed batches: T <= B * Nq (each sequence is at most Nq long)
+  if (workspace_bytes < fa_bwd_workspace_size(B * Nq, Hq, d)) return FA_ERR_INVALID_ARG;
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = static_cast<float*>(workspace);
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.group = Hq / Hkv;
+  p.causal = causal;
+  p.window = window;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return fa::launch_bwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK:
+      return "FA_OK";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: unsupported configuration";
+    case FA_ERR_HIP:
+      return "FA_ERR_HIP: HIP runtime error";
+    default:
+      return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels:
+// MFMA operand types, LDS tile addressing, work-group -> tile mapping and the
+// per-sequence geometry of dense and packed batches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_params.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] * B[16x32].
+// Operand layout per lane l (wave64):  A row m = l % 32, B column n = l % 32;
+// both hold 8 consecutive K slots selected by l / 32.  The result holds
+// column n = l % 32 and rows 8*(i/4) + 4*(l/32) + i%4 for i = 0..15.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b,
+                                         const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Round 8 floats to bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2,
+                                              float a3, float a4, float a5,
+                                              float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+
+// Value of lane (l ^ 32): the other half of the wave.
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// ---------------------------------------------------------------- LDS tiles
+// A K or V tile of R rows x D bf16 columns is stored row-major with its
+// 16-byte chunks permuted inside each row: chunk c of row r lives at chunk
+// c ^ swz(r).  swz maps any 8 consecutive rows (aligned) to distinct chunk
+// offsets and any 4 consecutive rows (aligned) to distinct 32-byte halves,
+// which keeps both access patterns below free of bank conflicts:
+//   * 128-bit reads of one chunk from 8 consecutive rows (MFMA A operand),
+//   * transposing 64-bit reads of 4 rows x 32 bytes (ds_read_b64_tr_b16).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Element offset of (row r, column col) in a swizzled tile with D columns.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz(r))) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ uint4 lds_read_b128(const __bf16* base, int off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address
+// of 4 consecutive bf16 (row j/4 of a 4-row block, columns 4*(j%4)..+3) and
+// receives column j of that 4 x 16 block (one element from each of the 4
+// rows).  Used to read V (or K, Q, dO) transposed for MFMA operands.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* base, int off) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (FA_LDS i16x4*)(base + off));
+  return __builtin_bit_cast(bf16x4, t);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Stages two [ROWS x D] bf16 tiles that share a row index (K and V, or Q and
+// dO) from global memory into swizzled LDS tiles, through registers so that
+// the global loads of the next tile can be in flight during compute.
+// Thread t covers 16-byte chunk t % (D/8) of rows t / (D/8) + pass * rows
+// per pass; rows at or past `limit` are written as zeros.
+template <int D, int ROWS, int THREADS>
+struct TilePairStager {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPP = THREADS / CPR;
+  static constexpr int PASSES = ROWS / RPP;
+  static_assert(ROWS % RPP == 0, "tile rows must be a multiple of rows per pass");
+  uint4 a[PASSES], b[PASSES];
+  int c, r;
+  __device__ __forceinline__ explicit TilePairStager(int tid)
+      : c(tid % CPR), r(tid / CPR) {}
+  __device__ __forceinline__ void load(const __bf16* ga, const __bf16* gb,
+                                       int64_t stride, int j0, int limit) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int j = j0 + r + ps * RPP;
+      if (j < limit) {
+        a[ps] = *reinterpret_cast<const uint4*>(ga + j * stride + c * 8);
+        b[ps] = *reinterpret_cast<const uint4*>(gb + j * stride + c * 8);
+      } else {
+        a[ps] = make_uint4(0, 0, 0, 0);
+        b[ps] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* la, __bf16* lb) const {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int row = r + ps * RPP;
+      const int off = row * D + ((c ^ swz(row)) << 3);
+      *reinterpret_cast<uint4*>(la + off) = a[ps];
+      *reinterpret_cast<uint4*>(lb + off) = b[ps];
+    }
+  }
+};
+
+// ---------------------------------------------------------------- grid
+// Work-groups are dispatched round-robin over the 8 XCDs (wg % 8), each with
+// its own L2.  Renumber them so that a contiguous range of logical ids runs
+// on one XCD: work that shares K/V (the query heads of one KV head) then
+// shares that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t wg, uint32_t n) {
+  uint32_t xcd = wg % kNumXcd, slot = wg / kNumXcd;
+  uint32_t per = n / kNumXcd, rem = n % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+// Rows of one sequence of a dense or packed batch.
+struct SeqSpan {
+  int64_t q0, k0;  // first token row of the sequence in Q and in K/V
+  int lq, lk;      // its query and key lengths
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int b, int nq,
+                                            int nk) {
+  SeqSpan s;
+  if (cu) {
+    int a = cu[b], e = cu[b + 1];
+    s.q0 = s.k0 = a;
+    s.lq = s.lk = e - a;
+  } else {
+    s.q0 = (int64_t)b * nq;
+    s.k0 = (int64_t)b * nk;
+    s.lq = nq;
+    s.lk = nk;
+  }
+  return s;
+}
+
+// Index of (head h, token row t of sequence b) in an LSE-shaped fp32 array:
+// dense [B, Hq, Nq], packed [Hq, T].
+__device__ __forceinline__ int64_t lse_index(const int32_t* cu, int B, int Hq,
+                                             int Nq, int b, int h, int64_t q0,
+                                             int i) {
+  if (cu) return (int64_t)h * cu[B] + q0 + i;
+  return ((int64_t)b * Hq + h) * Nq + i;
+}
+
+// Visibility of key j from query i (sequence-relative), delta = lk - lq.
+template <bool CAUSAL, bool WINDOW>
+__device__ __forceinline__ bool visible(int i, int j, int delta, int lk,
+                                        int window) {
+  bool ok = j < lk;
+  if (CAUSAL) ok = ok && (j <= i + delta);
+  if (WINDOW) ok = ok && (i + delta - j < window);
+  return ok;
+}
+
+}  // namespace fa

@@ -1,0 +1,292 @@
+// Exact attention forward, bf16 in / bf16 out, fp32 softmax state, gfx950.
+//
+// Method (llms.blog "FlashAttention: How IO-Aware Tiling and Online Softmax
+// Solved Transformer Memory Bottlenecks"):
+//   * "1. IO-Aware Tiling": a work-group owns a block of query rows and
+//     visits the key/value blocks; only the final output block is written.
+//   * "2. Online Softmax Reduction": per query row a running maximum m, a
+//     running normaliser l and an unnormalised output accumulator are
+//     rescaled whenever m grows, and O = acc / l once at the end.
+//   * "FlashAttention-2: Parallelism Across the Sequence Dimension": the
+//     grid runs over (batch, head, query block); exp is taken as exp2 with
+//     the scale folded in and the division by l is done once.
+//
+// gfx950 mapping (one work-group = 4 waves x 32 query rows = 128 rows):
+//   * The whole computation is done transposed so that every lane owns one
+//     query row from start to end:  S^T = K Q^T  and  O^T += V^T P^T, both
+//     on v_mfma_f32_32x32x16_bf16.  In the S^T result lane l holds query
+//     l % 32 and 16 of the 32 keys of a block; the other 16 keys of the same
+//     query sit in lane l ^ 32.  Row max therefore needs one cross-half
+//     exchange per tile, and the row sum none until the epilogue.
+//   * The exponentiated scores already sit in the B-operand layout of the
+//     P*V product (after bf16 rounding), so P never leaves registers.  The
+//     key order inside each 16-key chunk is permuted identically in P and in
+//     the transposed V reads (ds_read_b64_tr_b16), which leaves the
+//     contraction unchanged.
+//   * Q fragments live in VGPRs for the whole kernel; K and V tiles of 64
+//     keys are staged through LDS with 128-bit loads, double buffered: the
+//     global loads of tile j+1 are in flight while tile j is computed.
+//   * Causal and window masks skip whole tiles; element masks are only
+//     evaluated on tiles that straddle a boundary.
+//   * Lazy rescaling: the running maximum used for exponentiation is only
+//     raised when a row's maximum grows by more than 2^8, so most tiles skip
+//     the accumulator rescale.  Scores stay <= 2^8 in fp32, and O and LSE
+//     are unchanged because l and acc always use the same reference.
+#include <type_traits>
+
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBM = 128;  // query rows per work-group
+constexpr int kBN = 64;   // keys per K/V tile
+constexpr int kThreads = 256;
+constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
+
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_bf16_kernel(FwdParams p) {
+  constexpr int KS = D / 16;            // k-steps of the QK^T contraction
+  constexpr int NB = kBN / 32;          // 32-key blocks per tile
+  constexpr int NC = kBN / 16;          // 16-key chunks per tile
+  constexpr int DB = D / 32;            // 32-column blocks of the output
+  constexpr float kInf = __builtin_inff();
+
+  __shared__ __attribute__((aligned(16))) __bf16 sk[2][kBN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sv[2][kBN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, r32 = lane & 31;
+
+  // ---- which (sequence, head, query block) this work-group computes
+  uint32_t id = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int G = p.group;
+  const int gi = id % G;
+  id /= G;
+  const int t_ord = id % p.num_qtiles;
+  id /= p.num_qtiles;
+  const int hkv = id % p.Hkv;
+  const int b = id / p.Hkv;
+  const int h = hkv * G + gi;
+  // causal: longest rows first so that the tail of the grid is short
+  const int qt = CAUSAL ? (p.num_qtiles - 1 - t_ord) : t_ord;
+  const SeqSpan sp = seq_span(VARLEN ? p.cu_seqlens : nullptr, b, p.Nq, p.Nk);
+  const int q_start = qt * kBM;
+  if (q_start >= sp.lq) return;
+  const int delta = sp.lk - sp.lq;
+  const int q_end = min(q_start + kBM, sp.lq);
+
+  int kv_lo = 0, kv_hi = sp.lk;
+  if (CAUSAL) kv_hi = min(kv_hi, q_end + delta);
+  if (WINDOW) kv_lo = max(0, q_start + delta - p.window + 1);
+  kv_lo = (kv_lo / kBN) * kBN;
+
+  const int64_t qstride = (int64_t)p.Hq * D;
+  const int64_t kstride = (int64_t)p.Hkv * D;
+  const __bf16* Kg = (const __bf16*)p.k + sp.k0 * kstride + (int64_t)hkv * D;
+  const __bf16* Vg = (const __bf16*)p.v + sp.k0 * kstride + (int64_t)hkv * D;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): query qi, 8 columns per step
+  const int qi = q_start + wave * 32 + r32;
+  bf16x8 qf[KS];
+  if (qi < sp.lq) {
+    const __bf16* qp = (const __bf16*)p.q + (sp.q0 + qi) * qstride +
+                       (int64_t)h * D + hl * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+
+  // ---- K/V staging (rows past lk are zero-filled)
+  TilePairStager<D, kBN, kThreads> stage(tid);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float m_run = -kInf;  // reference maximum, scaled (log2) units
+  float l_run = 0.f;    // this half-wave's share of the normaliser
+  const float c = p.scale_log2;
+
+  const int qlo_w = q_start + wave * 32;
+  const int qhi_w = min(qlo_w + 31, sp.lq - 1);
+
+  int buf = 0;
+  if (kv_lo < kv_hi) stage.load(Kg, Vg, kstride, kv_lo, sp.lk);
+  for (int j0 = kv_lo; j0 < kv_hi; j0 += kBN) {
+    stage.store(sk[buf], sv[buf]);
+    __syncthreads();
+    if (j0 + kBN < kv_hi) stage.load(Kg, Vg, kstride, j0 + kBN, sp.lk);
+
+    bool active = qlo_w <= qhi_w;
+    if (CAUSAL) active = active && (j0 <= qhi_w + delta);
+    if (WINDOW) active = active && (j0 + kBN - 1 > qlo_w + delta - p.window);
+    if (active) {
+      const __bf16* kt = sk[buf];
+      const __bf16* vt = sv[buf];
+      bool need_mask = (j0 + kBN > sp.lk);
+      if (CAUSAL) need_mask = need_mask || (j0 + kBN - 1 > qlo_w + delta);
+      if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
+
+      // S^T block kb: rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4, col = qi
+      f32x16 s[NB];
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          uint4 a = lds_read_b128(kt, tile_off<D>(kb * 32 + r32, st * 16 + hl * 8));
+          s[kb] = mfma32(as_bf16x8(a), qf[st], s[kb]);
+        }
+      }
+
+      // Online-softmax update of this tile.  MASKED tiles straddle a mask
+      // boundary: invisible scores are replaced by a sentinel that never wins
+      // the row extreme, and their probabilities are forced to zero.
+      auto softmax_tile = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        uint32_t vis = 0xffffffffu;  // bit kb*16+i: key visible
+        if (MASKED) {
+          vis = 0;
+          const float sentinel = (c >= 0.f) ? -kInf : kInf;
+#pragma unroll
+          for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+              const bool ok = visible<CAUSAL, WINDOW>(qi, j, delta, sp.lk, p.window);
+              vis |= (ok ? 1u : 0u) << (kb * 16 + i);
+              s[kb][i] = ok ? s[kb][i] : sentinel;
+            }
+        }
+        // row extreme of the raw scores (max for c >= 0, min for c < 0)
+        float rm;
+        if (c >= 0.f) {
+          rm = s[0][0];
+#pragma unroll
+          for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rm = fmaxf(rm, s[kb][i]);
+          rm = fmaxf(rm, xor32(rm));
+        } else {
+          rm = s[0][0];
+#pragma unroll
+          for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rm = fminf(rm, s[kb][i]);
+          rm = fminf(rm, xor32(rm));
+        }
+        const float tmax = __builtin_isinf(rm) ? -kInf : rm * c;
+
+        float m_use = m_run;
+        if (tmax > m_run + kRescaleSlack) m_use = tmax;  // also when m_run = -inf
+        const float m_sub = (m_use == -kInf) ? 0.f : m_use;
+        const float alpha = fast_exp2(m_run - m_sub);  // exactly 1 when unchanged
+        m_run = m_use;
+        l_run *= alpha;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
+
+        const float neg = -m_sub;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(fmaf(s[kb][i], c, neg));
+            if (MASKED) pv = ((vis >> (kb * 16 + i)) & 1) ? pv : 0.f;
+            l_run += pv;
+            s[kb][i] = pv;
+          }
+      };
+      if (need_mask)
+        softmax_tile(std::true_type{});
+      else
+        softmax_tile(std::false_type{});
+
+      // O^T[d][q] += sum_j V[j][d] P[q][j]; 16-key chunk kc holds keys
+      // 16kc + 4hl + {0..3} (slots 0..3) and 16kc + 8 + 4hl + {0..3} (4..7)
+      const int tr_row = 4 * hl + ((lane & 15) >> 2);
+      const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+#pragma unroll
+      for (int kc = 0; kc < NC; ++kc) {
+        const int kb = kc >> 1, i0 = (kc & 1) * 8;
+        const bf16x8 pb = pack_bf16x8(s[kb][i0 + 0], s[kb][i0 + 1], s[kb][i0 + 2],
+                                      s[kb][i0 + 3], s[kb][i0 + 4], s[kb][i0 + 5],
+                                      s[kb][i0 + 6], s[kb][i0 + 7]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int col = db * 32 + tr_col;
+          const bf16x4 lo = lds_read_tr(vt, tile_off<D>(16 * kc + tr_row, col));
+          const bf16x4 hi = lds_read_tr(vt, tile_off<D>(16 * kc + 8 + tr_row, col));
+          acc[db] = mfma32(cat(lo, hi), pb, acc[db]);
+        }
+      }
+    }
+    buf ^= 1;
+  }
+
+  // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
+  const float l_tot = l_run + xor32(l_run);
+  if (qi < sp.lq) {
+    const float inv = (l_tot == 0.f) ? 0.f : 1.0f / l_tot;
+    __bf16* op = (__bf16*)p.o + (sp.q0 + qi) * qstride + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bf16x4 w;
+        w[0] = (__bf16)(acc[db][4 * r + 0] * inv);
+        w[1] = (__bf16)(acc[db][4 * r + 1] * inv);
+        w[2] = (__bf16)(acc[db][4 * r + 2] * inv);
+        w[3] = (__bf16)(acc[db][4 * r + 3] * inv);
+        *reinterpret_cast<uint2*>(op + db * 32 + r * 8 + hl * 4) =
+            __builtin_bit_cast(uint2, w);
+      }
+    if (hl == 0) {
+      const float m_sub = (m_run == -kInf) ? 0.f : m_run;
+      const float lse = (l_tot == 0.f) ? -kInf : (m_sub + __log2f(l_tot)) * kLn2;
+      p.lse[lse_index(VARLEN ? p.cu_seqlens : nullptr, p.B, p.Hq, p.Nq, b, h,
+                      sp.q0, qi)] = lse;
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool WINDOW>
+hipError_t launch3(const FwdParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)p.B * p.Hq * p.num_qtiles), block(kThreads);
+  if (p.cu_seqlens)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WINDOW, true>), grid, block, 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WINDOW, false>), grid, block, 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  const bool win = p.window > 0;
+  if (p.causal)
+    return win ? launch3<D, true, true>(p, stream) : launch3<D, true, false>(p, stream);
+  return win ? launch3<D, false, true>(p, stream) : launch3<D, false, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdParams& p_in, hipStream_t stream) {
+  FwdParams p = p_in;
+  p.num_qtiles = (p.Nq + kBM - 1) / kBM;
+  return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+}
+
+}  // namespace fa

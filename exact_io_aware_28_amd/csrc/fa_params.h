@@ -1,0 +1,52 @@
+// Host/device parameter blocks and the internal launcher interface between
+// the C-ABI layer (fa_api.hip) and the kernel files.  Not part of the public
+// ABI: the public header is include/fa_mi355x.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// One forward call, already validated.  Offsets are computed in the kernels
+// from the token-major layouts documented in the public header.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_seqlens;  // nullptr for dense batches
+  int B, Hq, Hkv, Nq, Nk, d;
+  int group;                  // Hq / Hkv
+  int causal, window;
+  float scale;                // multiplier of Q K^T
+  float scale_log2;           // scale * log2(e): exp(x*scale) = exp2(x*scale_log2)
+  int num_qtiles;             // ceil(Nq / query-tile rows) of the kernel
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;               // workspace: D_i = sum_c dO_ic O_ic, LSE layout
+  const int32_t* cu_seqlens;
+  int B, Hq, Hkv, Nq, Nk, d;
+  int group;
+  int causal, window;
+  float scale;
+  float scale_log2;
+};
+
+// Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+
+}  // namespace fa

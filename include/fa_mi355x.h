@@ -1,0 +1,147 @@
+/*
+ * fa_mi355x.h - C ABI of libfa_mi355x: exact IO-aware attention on MI355X
+ * (gfx950, CDNA4).
+ *
+ * What is computed.  For every (sequence, query head h):
+ *     S = scale * Q_h K_g^T,   P = softmax(S + mask),   O_h = P V_g,
+ *     LSE_h[i] = ln sum_j exp(S_ij + mask_ij),
+ * with g = h / (Hq / Hkv) the KV head shared by a contiguous group of query
+ * heads (GQA; Hkv = 1 is MQA).  The result is the plain softmax attention,
+ * computed tile by tile with the online-softmax recurrence so that no N x N
+ * score or probability matrix ever reaches device memory.
+ *   - S, P, O: llms.blog "FlashAttention: How IO-Aware Tiling and Online
+ *     Softmax Solved Transformer Memory Bottlenecks", "Naive Attention
+ *     Execution Profile"; tiling and the running (m, l, O) state: same page,
+ *     "1. IO-Aware Tiling" and "2. Online Softmax Reduction".
+ *   - logsumexp saved for a recomputing backward: tokrepo.com "Flash
+ *     Attention - Fast Memory-Efficient Exact Attention", "Architecture
+ *     Overview"; the backward that reloads Q, K, V tiles and recomputes the
+ *     scores: llms.blog page, "3. Recomputation in the Backward Pass".
+ *   - causal, sliding-window, variable-length and GQA/MQA: tokrepo.com page,
+ *     "What Flash Attention Does" and "Key Features".
+ *
+ * Mask conventions (the pages fix none; these are this library's readings):
+ *   - causal != 0: query i sees key j only if j <= i + (Nk - Nq)
+ *     (bottom-right aligned; for Nq == Nk the usual lower triangle);
+ *   - window > 0: query i sees key j only if (i + Nk - Nq) - j < window,
+ *     i.e. at most `window` keys counting itself; window == 0: no window;
+ *   - packed batches (cu_seqlens != NULL): a query sees only keys of its own
+ *     sequence, and sequence positions start at 0 in each sequence;
+ *   - a query that sees no key gets O = 0 and LSE = -inf.
+ *
+ * Layouts (all tensors dense and contiguous, head dimension innermost):
+ *   dense  (cu_seqlens == NULL): Q, O [B, Nq, Hq, d];  K, V [B, Nk, Hkv, d];
+ *                                LSE [B, Hq, Nq] fp32
+ *   packed (cu_seqlens != NULL): Q, O [T, Hq, d];  K, V [T, Hkv, d];
+ *                                LSE [Hq, T] fp32,  T = cu_seqlens[B]
+ *     cu_seqlens: device int32[B + 1], nondecreasing prefix sums of the B
+ *     sequence lengths, cu_seqlens[0] == 0; Q and K share it (self-attention),
+ *     Nq == Nk must be >= every sequence length (it sizes the launch grid).
+ *   dq, dk, dv have the layouts of q, k, v.
+ *
+ * Ownership and execution.  Every buffer is owned by the caller and lives in
+ * device memory (HBM) unless stated otherwise.  The library never allocates,
+ * frees or synchronises, and keeps no mutable global state: calls are thread
+ * safe and only enqueue work on `stream` (a hipStream_t; NULL = the null
+ * stream) before returning.  Inputs are read-only; outputs are fully
+ * overwritten, never accumulated into.  Results are deterministic: the same
+ * inputs give the same bits.
+ *
+ * Errors.  Each entry point returns an fa_status.  Argument checks happen on
+ * the host before any HIP call, so a call that returns FA_ERR_INVALID_ARG or
+ * FA_ERR_UNSUPPORTED has enqueued nothing.  FA_ERR_HIP reports a failed
+ * launch (hipGetLastError).  Device-side errors cannot be detected: a
+ * malformed cu_seqlens (decreasing, or sequences longer than Nq, or a total
+ * larger than the buffers) is undefined behaviour.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, bad scale */
+  FA_ERR_UNSUPPORTED = 2,  /* valid request this library does not implement */
+  FA_ERR_HIP = 3           /* the HIP runtime rejected a launch */
+} fa_status;
+
+/*
+ * Forward, bf16 inputs and output, fp32 LSE.
+ *   q, k, v : bf16 (raw bits, 2 bytes per element), layouts above
+ *   o       : bf16 output, layout of q, rounded to nearest even
+ *   lse     : fp32 output, natural-log logsumexp of the scaled, masked scores
+ *   B       : batch size (dense) or number of sequences (packed), >= 1
+ *   Hq, Hkv : query / KV heads, >= 1, Hq % Hkv == 0
+ *   Nq, Nk  : query / key sequence lengths (packed: the longest sequence,
+ *             and Nq == Nk), >= 1
+ *   d       : head dimension, 64 or 128
+ *   scale   : finite multiplier of Q K^T (usually 1/sqrt(d))
+ *   causal  : 0 or 1
+ *   window  : 0 = none, > 0 = keys visible per query counting itself
+ *   cu_seqlens : NULL (dense) or device int32[B + 1] (packed)
+ * Pointers q, k, v, o must be 16-byte aligned; lse 4-byte aligned.
+ * Returns FA_ERR_INVALID_ARG for a null or misaligned pointer, a size < 1,
+ * Hq % Hkv != 0, a non-finite scale, causal not in {0,1}, window < 0;
+ * FA_ERR_UNSUPPORTED for d not in {64, 128}, or packed with Nq != Nk.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d,
+           float scale, int causal, int window,
+           const int32_t* cu_seqlens, void* stream);
+
+/*
+ * Forward with fp32 q, k, v, o (same arguments, layouts and errors as
+ * fa_fwd, with 4 bytes per element).  Scores, softmax and the output
+ * accumulator are computed in fp32 on the vector ALUs.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               float scale, int causal, int window,
+               const int32_t* cu_seqlens, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for T_q = B * Nq query rows and Hq
+ * heads (for packed batches B * Nq bounds cu_seqlens[B], which the host
+ * cannot read).  O(T_q * Hq), never quadratic in the sequence length.  d is
+ * accepted for future layouts.  Returns 0 for a negative or zero argument.
+ */
+size_t fa_bwd_workspace_size(int T_q, int Hq, int d);
+
+/*
+ * Backward by recomputation (bf16 in, bf16 out).
+ *   q, k, v, o, dout : bf16, layouts above; o is the output of fa_fwd for the
+ *                      same q, k, v and arguments
+ *   lse              : fp32, the LSE written by that fa_fwd call
+ *   dq, dk, dv       : bf16 outputs, fully overwritten; for GQA, dk and dv
+ *                      of a KV head sum over its query-head group
+ *   workspace        : device buffer of at least
+ *                      fa_bwd_workspace_size(B * Nq, Hq, d) bytes, 16-byte
+ *                      aligned, used as scratch (contents undefined after the
+ *                      call); it must not alias any other argument
+ * The backward recomputes P = exp(S - LSE) tile by tile and forms
+ * D_i = sum_c dO_ic O_ic, dS = P (dP - D); dQ = scale dS K, dK = scale dS^T Q,
+ * dV = P^T dO, with no N x N buffer.
+ * Errors as fa_fwd, plus FA_ERR_INVALID_ARG when the workspace is NULL or
+ * smaller than required.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d,
+           float scale, int causal, int window,
+           const int32_t* cu_seqlens, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

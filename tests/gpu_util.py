@@ -1,0 +1,112 @@
+"""Helpers shared by the GPU parity tests: moving the seeded inputs to the
+device, calling the library through its binding, and the error metrics with
+the tolerances the parity bar states."""
+
+import math
+import sys
+
+import numpy as np
+
+# Parity bar (bf16 path): O max |err| <= 2e-2 and mean |err| <= 2e-3 over all
+# compared elements; LSE |err| <= 1e-3; each of dQ, dK, dV:
+# max |err| <= 5e-2 * max |reference|.
+O_MAX, O_MEAN, LSE_MAX, GRAD_REL = 2e-2, 2e-3, 1e-3, 5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, dtype="bf16"):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)
+    return t.cuda()
+
+
+def to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def run_fwd(inp):
+    """Call fa_fwd (or fa_fwd_f32) on a workloads.make_inputs() dict."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    dt = inp.get("dtype", "bf16")
+    q, k, v = (to_dev(inp[n], dt) for n in ("q", "k", "v"))
+    cu = inp.get("cu_seqlens")
+    cu_t = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    fn = fa.fa_fwd if dt == "bf16" else fa.fa_fwd_f32
+    o, lse = fn(q, k, v, scale=inp["scale"], causal=inp["causal"], window=inp["window"],
+                cu_seqlens=cu_t, max_seqlen=inp.get("Nq") if cu is not None else None)
+    torch.cuda.synchronize()
+    return dict(q=q, k=k, v=v, o=o, lse=lse, cu=cu_t)
+
+
+def run_bwd(inp, dev):
+    import torch
+    import exact_io_aware_28_amd as fa
+    do = to_dev(inp["do"])
+    cu = dev["cu"]
+    dq, dk, dv = fa.fa_bwd(dev["q"], dev["k"], dev["v"], dev["o"], do, dev["lse"],
+                           scale=inp["scale"], causal=inp["causal"], window=inp["window"],
+                           cu_seqlens=cu, max_seqlen=inp.get("Nq") if cu is not None else None)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def o_errors(o, ref):
+    err = np.abs(o - ref)
+    return float(err.max()), float(err.mean())
+
+
+def check_o(o, ref, what=""):
+    mx, mn = o_errors(o, ref)
+    say(f"  {what} O max|err|={mx:.3e} mean|err|={mn:.3e}")
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    assert mx <= O_MAX and mn <= O_MEAN, (what, mx, mn)
+    return mx, mn
+
+
+def check_lse(lse, ref, what=""):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref)), f"{what}: -inf pattern"
+    mx = float(np.abs(lse[fin] - ref[fin]).max()) if fin.any() else 0.0
+    say(f"  {what} LSE max|err|={mx:.3e}")
+    assert mx <= LSE_MAX, (what, mx)
+    return mx
+
+
+def check_grad(g, ref, what=""):
+    scale = float(np.abs(ref).max())
+    mx = float(np.abs(g - ref).max())
+    say(f"  {what} max|err|={mx:.3e} max|ref|={scale:.3e} rel={mx / max(scale, 1e-30):.3e}")
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    assert mx <= GRAD_REL * scale, (what, mx, scale)
+    return mx / max(scale, 1e-30)
+
+
+def sample_rows(n, tile=128, count=48, seed=0):
+    """Rows that cover the first and last rows, tile edges and random rows."""
+    rng = np.random.default_rng(seed)
+    s = {0, 1, n - 1, n - 2}
+    for t in range(tile, n, tile):
+        if len(s) > count // 2:
+            break
+        s.update({t - 1, t})
+    s.update(rng.integers(0, n, size=count - len(s) if count > len(s) else 0).tolist())
+    return np.array(sorted(x for x in s if 0 <= x < n))
+
+
+def attention_flops(B, Hq, Nq, Nk, d, causal):
+    f = 4.0 * B * Hq * Nq * Nk * d
+    return f / 2 if causal else f
+
+
+def is_close_bits(a, b):
+    return a.shape == b.shape and bool((a == b).all())
+
+
+__all__ = ["say", "to_dev", "to_np", "run_fwd", "run_bwd", "check_o", "check_lse",
+           "check_grad", "sample_rows", "math"]

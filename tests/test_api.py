@@ -1,0 +1,139 @@
+"""CPU tests of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before any HIP call (no GPU needed:
+a rejected call enqueues nothing, so fake device addresses are safe here)."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import exact_io_aware_28_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH),
+                                reason="library not built")
+
+# fake, 16-byte aligned device addresses: never dereferenced on these paths
+P = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(12)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
+                                    "fa_fwd_f32", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    L = fa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    if shutil.which("nm"):
+        out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH],
+                             capture_output=True, text=True).stdout
+        exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+        assert set(declared_functions()) <= exported
+
+
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_is_self_contained(lang, tmp_path):
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text('#include "fa_mi355x.h"\n'
+                   'int (*f)(const void*, const void*, const void*, void*, float*, int,'
+                   ' int, int, int, int, int, float, int, int, const int32_t*, void*)'
+                   ' = fa_fwd;\nint main(void){return f == 0;}\n')
+    r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-I",
+                        os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _fwd(fn=None, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, Hq=4, Hkv=2, Nq=64,
+         Nk=64, d=128, scale=0.125, causal=0, window=0, cu=None):
+    fn = fn or fa.lib().fa_fwd
+    return fn(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window, cu, None)
+
+
+BAD_FWD = [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(q=ctypes.c_void_p(0x10008)), fa.FA_ERR_INVALID_ARG),   # misaligned
+    (dict(lse=ctypes.c_void_p(0x10002)), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(window=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(cu=P[5], Nq=64, Nk=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(cu=ctypes.c_void_p(0x10001)), fa.FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("bad,code", BAD_FWD)
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+def test_forward_rejects(entry, bad, code):
+    assert _fwd(getattr(fa.lib(), entry), **bad) == code
+
+
+def _bwd(ws=P[9], ws_bytes=None, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7],
+             dv=P[8], B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125, causal=0,
+             window=0, cu=None)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_size(a["B"] * a["Nq"], a["Hq"], a["d"])
+    return fa.lib().fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                           a["dk"], a["dv"], ws, ws_bytes, a["B"], a["Hq"], a["Hkv"],
+                           a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                           a["window"], a["cu"], None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(ws=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=None), fa.FA_ERR_INVALID_ARG),
+    (dict(do=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=ctypes.c_void_p(0x20004)), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(window=-3), fa.FA_ERR_INVALID_ARG),
+])
+def test_backward_rejects(bad, code):
+    assert _bwd(**bad) == code
+
+
+def test_workspace_is_linear_in_rows():
+    s1 = fa.fa_bwd_workspace_size(16384, 16, 128)
+    s2 = fa.fa_bwd_workspace_size(32768, 16, 128)
+    assert s1 >= 16384 * 16 * 4 and s2 <= 2 * s1 + 256
+    assert fa.fa_bwd_workspace_size(0, 16, 128) == 0
+    assert fa.fa_bwd_workspace_size(10, -1, 128) == 0
+
+
+def test_status_strings():
+    for st in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+        assert fa.fa_status_string(st).startswith("FA_")
+    assert "unknown" in fa.fa_status_string(99)
