@@ -130,6 +130,71 @@ struct TilePairStager {
   }
 };
 
+// ---------------------------------------------------------------- LDS DMA
+// Buffer loads that write straight into LDS (buffer_load_dwordx4 ... lds):
+// lane l of a wave deposits its 16 bytes at lds_base + 16 l, so one wave
+// instruction fills 1 KB of LDS.  The buffer descriptor bounds every access:
+// a lane whose offset is past num_records reads zeros, which is how rows
+// beyond the end of a sequence are zero-filled without a branch.
+constexpr int kBufferRsrcWord3 = 0x00020000;  // gfx9-family raw buffer, 32-bit data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_bytes,
+                                           kBufferRsrcWord3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, __bf16* lds_base,
+                                      uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds_base, 16, (int)voffset,
+                                           0, 0, 0);
+}
+
+// Per-lane byte offsets for staging a [ROWS x D] bf16 tile whose rows are
+// `stride_bytes` apart in global memory into a swizzled LDS tile with
+// WAVES waves.  Wave w issues instructions w*PER_WAVE .. +PER_WAVE-1; each
+// instruction covers 1024 / (2 D) consecutive rows of the LDS tile, and lane
+// l fills physical chunk l % (D/8) of its row, i.e. logical chunk
+// (l % (D/8)) ^ swz(row).
+template <int D, int ROWS, int WAVES>
+struct TileDma {
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunks;     // rows per 1 KB instruction
+  static constexpr int kInsts = ROWS / kRowsPerInst;    // instructions per tile
+  static constexpr int kPerWave = kInsts / WAVES;
+  static_assert(kInsts % WAVES == 0, "tile must split evenly over the waves");
+  uint32_t voff[kPerWave];
+  int first;  // first instruction index of this wave
+  __device__ __forceinline__ TileDma(int wave, int lane, uint32_t stride_bytes) {
+    first = wave * kPerWave;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int row = (first + i) * kRowsPerInst + lane / kChunks;
+      const int chunk = (lane % kChunks) ^ swz(row);
+      voff[i] = (uint32_t)row * stride_bytes + (uint32_t)chunk * 16u;
+    }
+  }
+  // Stage rows [j0, j0 + ROWS) of a tensor whose row 0 is at `g`; rows at or
+  // past `limit` read as zero.
+  __device__ __forceinline__ void issue(const __bf16* g, uint32_t stride_bytes, int j0,
+                                        int limit, __bf16* lds) const {
+    const int valid = limit - j0;  // >= 1 inside the loops that call this
+    const uint32_t nbytes = (uint32_t)(valid - 1) * stride_bytes + (uint32_t)D * 2u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(g + (int64_t)j0 * (stride_bytes / 2), nbytes);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) dma16(r, lds + (first + i) * 512, voff[i]);
+  }
+};
+
+// Barrier that publishes LDS-DMA data to the whole work-group: every wave
+// first waits for its own outstanding buffer->LDS loads (vmcnt 0), then all
+// waves meet.  The compiler's automatic waits only order a wave's reads after
+// its own loads, which is not enough when other waves' loads fill the tile.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- grid
 // Work-groups are dispatched round-robin over the 8 XCDs (wg % 8), each with
 // its own L2.  Renumber them so that a contiguous range of logical ids runs

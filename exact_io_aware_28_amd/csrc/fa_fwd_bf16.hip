@@ -23,9 +23,11 @@
 //     key order inside each 16-key chunk is permuted identically in P and in
 //     the transposed V reads (ds_read_b64_tr_b16), which leaves the
 //     contraction unchanged.
-//   * Q fragments live in VGPRs for the whole kernel; K and V tiles of 64
-//     keys are staged through LDS with 128-bit loads, double buffered: the
-//     global loads of tile j+1 are in flight while tile j is computed.
+//   * Q fragments live in VGPRs for the whole kernel.  K and V tiles of 64
+//     keys go from HBM/L2 straight into LDS (buffer loads with the LDS
+//     destination), two buffers: the loads of tile j+1 are issued right
+//     after the barrier that opens tile j and land while tile j is computed.
+//     Rows past the sequence end read as zeros (descriptor bounds check).
 //   * Causal and window masks skip whole tiles; element masks are only
 //     evaluated on tiles that straddle a boundary.
 //   * Lazy rescaling: the running maximum used for exponentiation is only
@@ -41,7 +43,8 @@ namespace {
 
 constexpr int kBM = 128;  // query rows per work-group
 constexpr int kBN = 64;   // keys per K/V tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
 
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN>
@@ -53,8 +56,12 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr int DB = D / 32;            // 32-column blocks of the output
   constexpr float kInf = __builtin_inff();
 
-  __shared__ __attribute__((aligned(16))) __bf16 sk[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sv[2][kBN * D];
+  // two K/V buffers as distinct objects, so that reads of one buffer are not
+  // ordered behind the loads still landing in the other
+  __shared__ __attribute__((aligned(1024))) __bf16 k0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 v0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 k1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 v1[kBN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, r32 = lane & 31;
@@ -84,8 +91,16 @@ void fwd_bf16_kernel(FwdParams p) {
 
   const int64_t qstride = (int64_t)p.Hq * D;
   const int64_t kstride = (int64_t)p.Hkv * D;
+  const uint32_t kstride_b = (uint32_t)(kstride * 2);
   const __bf16* Kg = (const __bf16*)p.k + sp.k0 * kstride + (int64_t)hkv * D;
   const __bf16* Vg = (const __bf16*)p.v + sp.k0 * kstride + (int64_t)hkv * D;
+
+  const TileDma<D, kBN, kWaves> dma(wave, lane, kstride_b);
+  auto issue = [&](int j0, __bf16* kb, __bf16* vb) {
+    dma.issue(Kg, kstride_b, j0, sp.lk, kb);
+    dma.issue(Vg, kstride_b, j0, sp.lk, vb);
+  };
+  if (kv_lo < kv_hi) issue(kv_lo, k0, v0);
 
   // ---- Q fragments (B operand of S^T = K Q^T): query qi, 8 columns per step
   const int qi = q_start + wave * 32 + r32;
@@ -101,9 +116,6 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int s = 0; s < KS; ++s) qf[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
-  // ---- K/V staging (rows past lk are zero-filled)
-  TilePairStager<D, kBN, kThreads> stage(tid);
-
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -115,124 +127,127 @@ void fwd_bf16_kernel(FwdParams p) {
 
   const int qlo_w = q_start + wave * 32;
   const int qhi_w = min(qlo_w + 31, sp.lq - 1);
+  // lane-dependent parts of the transposed V read address
+  const int tr_row = 4 * hl + ((lane & 15) >> 2);
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
-  int buf = 0;
-  if (kv_lo < kv_hi) stage.load(Kg, Vg, kstride, kv_lo, sp.lk);
-  for (int j0 = kv_lo; j0 < kv_hi; j0 += kBN) {
-    stage.store(sk[buf], sv[buf]);
-    __syncthreads();
-    if (j0 + kBN < kv_hi) stage.load(Kg, Vg, kstride, j0 + kBN, sp.lk);
-
+  auto compute = [&](int j0, const __bf16* kt, const __bf16* vt) {
     bool active = qlo_w <= qhi_w;
     if (CAUSAL) active = active && (j0 <= qhi_w + delta);
     if (WINDOW) active = active && (j0 + kBN - 1 > qlo_w + delta - p.window);
-    if (active) {
-      const __bf16* kt = sk[buf];
-      const __bf16* vt = sv[buf];
-      bool need_mask = (j0 + kBN > sp.lk);
-      if (CAUSAL) need_mask = need_mask || (j0 + kBN - 1 > qlo_w + delta);
-      if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
+    if (!active) return;
+    bool need_mask = (j0 + kBN > sp.lk);
+    if (CAUSAL) need_mask = need_mask || (j0 + kBN - 1 > qlo_w + delta);
+    if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
 
-      // S^T block kb: rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4, col = qi
-      f32x16 s[NB];
+    // S^T block kb: rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4, col = qi
+    f32x16 s[NB];
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
+    for (int kb = 0; kb < NB; ++kb) {
+      uint4 a[KS];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+      for (int st = 0; st < KS; ++st)
+        a[st] = lds_read_b128(kt, tile_off<D>(kb * 32 + r32, st * 16 + hl * 8));
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          uint4 a = lds_read_b128(kt, tile_off<D>(kb * 32 + r32, st * 16 + hl * 8));
-          s[kb] = mfma32(as_bf16x8(a), qf[st], s[kb]);
-        }
-      }
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) s[kb] = mfma32(as_bf16x8(a[st]), qf[st], s[kb]);
+    }
 
-      // Online-softmax update of this tile.  MASKED tiles straddle a mask
-      // boundary: invisible scores are replaced by a sentinel that never wins
-      // the row extreme, and their probabilities are forced to zero.
-      auto softmax_tile = [&](auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        uint32_t vis = 0xffffffffu;  // bit kb*16+i: key visible
-        if (MASKED) {
-          vis = 0;
-          const float sentinel = (c >= 0.f) ? -kInf : kInf;
-#pragma unroll
-          for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-              const bool ok = visible<CAUSAL, WINDOW>(qi, j, delta, sp.lk, p.window);
-              vis |= (ok ? 1u : 0u) << (kb * 16 + i);
-              s[kb][i] = ok ? s[kb][i] : sentinel;
-            }
-        }
-        // row extreme of the raw scores (max for c >= 0, min for c < 0)
-        float rm;
-        if (c >= 0.f) {
-          rm = s[0][0];
-#pragma unroll
-          for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) rm = fmaxf(rm, s[kb][i]);
-          rm = fmaxf(rm, xor32(rm));
-        } else {
-          rm = s[0][0];
-#pragma unroll
-          for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) rm = fminf(rm, s[kb][i]);
-          rm = fminf(rm, xor32(rm));
-        }
-        const float tmax = __builtin_isinf(rm) ? -kInf : rm * c;
-
-        float m_use = m_run;
-        if (tmax > m_run + kRescaleSlack) m_use = tmax;  // also when m_run = -inf
-        const float m_sub = (m_use == -kInf) ? 0.f : m_use;
-        const float alpha = fast_exp2(m_run - m_sub);  // exactly 1 when unchanged
-        m_run = m_use;
-        l_run *= alpha;
-        if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        }
-
-        const float neg = -m_sub;
+    // Online-softmax update and P V product.  MASKED tiles straddle a mask
+    // boundary: an invisible score is replaced by a sentinel that never wins
+    // the row extreme, and its probability is forced to zero.
+    auto softmax_tile = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const float sentinel = (c >= 0.f) ? -kInf : kInf;
+      auto key_of = [&](int kb, int i) { return j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3); };
+      if (MASKED) {
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float pv = fast_exp2(fmaf(s[kb][i], c, neg));
-            if (MASKED) pv = ((vis >> (kb * 16 + i)) & 1) ? pv : 0.f;
-            l_run += pv;
-            s[kb][i] = pv;
-          }
-      };
-      if (need_mask)
-        softmax_tile(std::true_type{});
-      else
-        softmax_tile(std::false_type{});
+          for (int i = 0; i < 16; ++i)
+            if (!visible<CAUSAL, WINDOW>(qi, key_of(kb, i), delta, sp.lk, p.window))
+              s[kb][i] = sentinel;
+      }
+      // row extreme of the raw scores (max for c >= 0, min for c < 0)
+      float rm = s[0][0];
+      if (c >= 0.f) {
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) rm = fmaxf(rm, s[kb][i]);
+        rm = fmaxf(rm, xor32(rm));
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) rm = fminf(rm, s[kb][i]);
+        rm = fminf(rm, xor32(rm));
+      }
+      const float tmax = __builtin_isinf(rm) ? -kInf : rm * c;
 
-      // O^T[d][q] += sum_j V[j][d] P[q][j]; 16-key chunk kc holds keys
+      float m_use = m_run;
+      if (tmax > m_run + kRescaleSlack) m_use = tmax;  // also when m_run = -inf
+      const float m_sub = (m_use == -kInf) ? 0.f : m_use;
+      const float alpha = fast_exp2(m_run - m_sub);  // exactly 1 when unchanged
+      m_run = m_use;
+      l_run *= alpha;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+
+      // exponentiate one 16-key chunk at a time and feed it straight to the
+      // P V product, so the chunk's MFMAs overlap the next chunk's exp2s:
+      // O^T[d][q] += sum_j V[j][d] P[q][j]; chunk kc holds keys
       // 16kc + 4hl + {0..3} (slots 0..3) and 16kc + 8 + 4hl + {0..3} (4..7)
-      const int tr_row = 4 * hl + ((lane & 15) >> 2);
-      const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      const float neg = -m_sub;
+      float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
       for (int kc = 0; kc < NC; ++kc) {
         const int kb = kc >> 1, i0 = (kc & 1) * 8;
-        const bf16x8 pb = pack_bf16x8(s[kb][i0 + 0], s[kb][i0 + 1], s[kb][i0 + 2],
-                                      s[kb][i0 + 3], s[kb][i0 + 4], s[kb][i0 + 5],
-                                      s[kb][i0 + 6], s[kb][i0 + 7]);
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = fast_exp2(fmaf(s[kb][i0 + e], c, neg));
+          if (MASKED)
+            pv[e] = visible<CAUSAL, WINDOW>(qi, key_of(kb, i0 + e), delta, sp.lk, p.window)
+                        ? pv[e] : 0.f;
+          if (e & 1)
+            lsum1 += pv[e];
+          else
+            lsum0 += pv[e];
+        }
+        const bf16x8 pb = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        bf16x8 va[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int col = db * 32 + tr_col;
-          const bf16x4 lo = lds_read_tr(vt, tile_off<D>(16 * kc + tr_row, col));
-          const bf16x4 hi = lds_read_tr(vt, tile_off<D>(16 * kc + 8 + tr_row, col));
-          acc[db] = mfma32(cat(lo, hi), pb, acc[db]);
+          va[db] = cat(lds_read_tr(vt, tile_off<D>(16 * kc + tr_row, col)),
+                       lds_read_tr(vt, tile_off<D>(16 * kc + 8 + tr_row, col)));
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(va[db], pb, acc[db]);
       }
-    }
-    buf ^= 1;
+      l_run += lsum0 + lsum1;
+    };
+    if (need_mask)
+      softmax_tile(std::true_type{});
+    else
+      softmax_tile(std::false_type{});
+  };
+
+  // ---- main loop over K/V tiles, two buffers (unrolled by two)
+  for (int j0 = kv_lo; j0 < kv_hi; j0 += 2 * kBN) {
+    dma_barrier();  // tile j0 is in buffer 0; buffer 1 is free
+    if (j0 + kBN < kv_hi) issue(j0 + kBN, k1, v1);
+    compute(j0, k0, v0);
+    if (j0 + kBN >= kv_hi) break;
+    dma_barrier();  // tile j0 + kBN is in buffer 1; buffer 0 is free
+    if (j0 + 2 * kBN < kv_hi) issue(j0 + 2 * kBN, k0, v0);
+    compute(j0 + kBN, k1, v1);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
