@@ -56,17 +56,32 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 // ---------------------------------------------------------------- LDS tiles
 // A K or V tile of R rows x D bf16 columns is stored row-major with its
 // 16-byte chunks permuted inside each row: chunk c of row r lives at chunk
-// c ^ swz(r).  swz maps any 8 consecutive rows (aligned) to distinct chunk
-// offsets and any 4 consecutive rows (aligned) to distinct 32-byte halves,
-// which keeps both access patterns below free of bank conflicts:
-//   * 128-bit reads of one chunk from 8 consecutive rows (MFMA A operand),
-//   * transposing 64-bit reads of 4 rows x 32 bytes (ds_read_b64_tr_b16).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// c ^ swz<D>(r).  The permutation is chosen (and checked exhaustively on the
+// host for 32- and 64-bank LDS) so that both access patterns below touch
+// distinct banks within every LDS pass:
+//   * 128-bit reads of one chunk from consecutive rows (MFMA A operand),
+//   * transposing 64-bit reads of 4 aligned rows x 32 bytes per 16 lanes
+//     (ds_read_b64_tr_b16), two such groups side by side per pass.
+// D = 128 (16 chunks): rows r..r+15 map one chunk to 16 distinct offsets,
+// and 4 aligned rows land in 4 distinct 64-byte groups.  D = 64 (8 chunks,
+// two rows per 256 bytes): same-parity rows of 16 map to distinct offsets.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    // bits 1..3 from r % 4 through the table {0, 6, 10, 12}, bit 0 = r/4 % 2,
+    // bit 3 also flipped by r/8 % 2
+    const int h = (0xCA60 >> ((r & 3) * 4)) & 0xF;
+    return h ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 3);
+  } else {
+    const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    return ((r1 ^ r3) << 2) | ((r0 ^ r2) << 1) | (r2 ^ r3);
+  }
+}
 
 // Element offset of (row r, column col) in a swizzled tile with D columns.
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int col) {
-  return r * D + ((((col >> 3) ^ swz(r))) << 3) + (col & 7);
+  return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
 }
 
 __device__ __forceinline__ uint4 lds_read_b128(const __bf16* base, int off) {
@@ -123,7 +138,7 @@ struct TilePairStager {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int row = r + ps * RPP;
-      const int off = row * D + ((c ^ swz(row)) << 3);
+      const int off = row * D + ((c ^ swz<D>(row)) << 3);
       *reinterpret_cast<uint4*>(la + off) = a[ps];
       *reinterpret_cast<uint4*>(lb + off) = b[ps];
     }
@@ -170,7 +185,7 @@ struct TileDma {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int row = (first + i) * kRowsPerInst + lane / kChunks;
-      const int chunk = (lane % kChunks) ^ swz(row);
+      const int chunk = (lane % kChunks) ^ swz<D>(row);
       voff[i] = (uint32_t)row * stride_bytes + (uint32_t)chunk * 16u;
     }
   }

@@ -52,6 +52,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int KS = D / 16;            // k-steps of the QK^T contraction
   constexpr int NB = kBN / 32;          // 32-key blocks per tile
+  constexpr int kPrefetch = (D == 128) ? 6 : 4;  // LDS reads ahead of the S MFMAs
   constexpr int NC = kBN / 16;          // 16-key chunks per tile
   constexpr int DB = D / 32;            // 32-column blocks of the output
   constexpr float kInf = __builtin_inff();
@@ -153,6 +154,16 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int st = 0; st < KS; ++st) s[kb] = mfma32(as_bf16x8(a[st]), qf[st], s[kb]);
     }
+    // Schedule: issue kPrefetch K-fragment reads before the first MFMA, then
+    // alternate one MFMA with one read, so several LDS reads stay in flight
+    // while the matrix core works (the default schedule keeps about two).
+    __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
+#pragma unroll
+    for (int i = 0; i < NB * KS - kPrefetch; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
 
     // Online-softmax update and P V product.  MASKED tiles straddle a mask
     // boundary: an invisible score is replaced by a sentinel that never wins
