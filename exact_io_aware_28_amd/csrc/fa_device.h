@@ -98,6 +98,26 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* base, int off) {
   return __builtin_bit_cast(bf16x4, t);
 }
 
+// The same two reads at a lane byte offset plus a byte offset that is a
+// compile-time constant after unrolling (whole rows, or a tile).  Keeping
+// the lane part in one register and the rest constant lets every read of a
+// tile reuse that register, with the constant in the instruction's offset
+// field; computing the full swizzled offset per read instead costs one
+// address register per distinct read.
+__device__ __forceinline__ uint4 lds_read_b128_at(const __bf16* base, uint32_t lane_off,
+                                                  uint32_t const_off) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(const FA_LDS u32x4*)((const FA_LDS char*)(const FA_LDS __bf16*)base +
+                                         lane_off + const_off);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr_at(const __bf16* base, uint32_t lane_off,
+                                                 uint32_t const_off) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (FA_LDS i16x4*)((FA_LDS char*)(FA_LDS __bf16*)base + lane_off + const_off));
+  return __builtin_bit_cast(bf16x4, t);
+}
+
 __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
   bf16x8 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
@@ -209,6 +229,10 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 }
+
+// ---------------------------------------------------------------- scheduling
+// Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 // ---------------------------------------------------------------- grid
 // Work-groups are dispatched round-robin over the 8 XCDs (wg % 8), each with

@@ -41,9 +41,9 @@
 namespace fa {
 namespace {
 
-constexpr int kBM = 128;  // query rows per work-group
-constexpr int kBN = 64;   // keys per K/V tile
 constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;  // query rows per work-group
+constexpr int kBN = 64;   // keys per K/V tile
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
 
@@ -131,6 +131,19 @@ void fwd_bf16_kernel(FwdParams p) {
   // lane-dependent parts of the transposed V read address
   const int tr_row = 4 * hl + ((lane & 15) >> 2);
   const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  // Lane byte offsets of the LDS reads inside a tile.  The swizzle depends
+  // on the low four row bits only, so 32-row blocks (K) and 16-row chunks
+  // (V) differ from these by whole rows, a constant that goes into the
+  // read instruction's offset field.
+  uint32_t koff[KS];     // K fragment, row r32, k-step st
+  uint32_t voff[2][DB];  // V transposed read, rows tr_row + 8h, column block db
+#pragma unroll
+  for (int st = 0; st < KS; ++st) koff[st] = 2 * tile_off<D>(r32, st * 16 + hl * 8);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      voff[h][db] = 2 * tile_off<D>(tr_row + 8 * h, db * 32 + tr_col);
 
   auto compute = [&](int j0, const __bf16* kt, const __bf16* vt) {
     bool active = qlo_w <= qhi_w;
@@ -148,7 +161,7 @@ void fwd_bf16_kernel(FwdParams p) {
       uint4 a[KS];
 #pragma unroll
       for (int st = 0; st < KS; ++st)
-        a[st] = lds_read_b128(kt, tile_off<D>(kb * 32 + r32, st * 16 + hl * 8));
+        a[st] = lds_read_b128_at(kt, koff[st], kb * 32 * D * 2);
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
@@ -157,13 +170,13 @@ void fwd_bf16_kernel(FwdParams p) {
     // Schedule: issue kPrefetch K-fragment reads before the first MFMA, then
     // alternate one MFMA with one read, so several LDS reads stay in flight
     // while the matrix core works (the default schedule keeps about two).
-    __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
 #pragma unroll
     for (int i = 0; i < NB * KS - kPrefetch; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
 
     // Online-softmax update and P V product.  MASKED tiles straddle a mask
     // boundary: an invisible score is replaced by a sentinel that never wins
@@ -235,9 +248,8 @@ void fwd_bf16_kernel(FwdParams p) {
         bf16x8 va[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + tr_col;
-          va[db] = cat(lds_read_tr(vt, tile_off<D>(16 * kc + tr_row, col)),
-                       lds_read_tr(vt, tile_off<D>(16 * kc + 8 + tr_row, col)));
+          va[db] = cat(lds_read_tr_at(vt, voff[0][db], 16 * kc * D * 2),
+                       lds_read_tr_at(vt, voff[1][db], 16 * kc * D * 2));
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = mfma32(va[db], pb, acc[db]);
