@@ -39,6 +39,7 @@ constexpr int kKeyBlock = 128;  // keys per dK/dV work-group (4 waves x 32)
 constexpr int kQTile = 64;      // query rows per staged tile in dK/dV
 constexpr int kQBlock = 128;    // query rows per dQ work-group (4 waves x 32)
 constexpr int kKTile = 64;      // keys per staged tile in dQ
+constexpr int kReadsAhead = 4;  // LDS fragment reads issued ahead of the score MFMAs
 
 // ------------------------------------------------------------ 1. D = dO . O
 template <int D>
@@ -70,15 +71,25 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ 2. dK, dV
+// dK and dV accumulators plus the resident K and V fragments take about 350
+// registers at d = 128 (one wave per SIMD); d = 64 fits two waves.
+template <int D>
+constexpr int dkdv_waves_per_simd() { return D == 64 ? 2 : 1; }
+
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(dkdv_waves_per_simd<D>())))
 void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
   constexpr int KS = D / 16, DB = D / 32, QB = kQTile / 32;
   constexpr float kInf = __builtin_inff();
-  __shared__ __attribute__((aligned(16))) __bf16 sq[2][kQTile * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sdo[2][kQTile * D];
-  __shared__ __attribute__((aligned(16))) float slse[2][kQTile];
-  __shared__ __attribute__((aligned(16))) float sdl[2][kQTile];
+  // two Q/dO buffers as distinct objects, so that reads of one buffer are
+  // not ordered behind the loads still landing in the other
+  __shared__ __attribute__((aligned(1024))) __bf16 sq0[kQTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sdo0[kQTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sq1[kQTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sdo1[kQTile * D];
+  __shared__ __attribute__((aligned(16))) float sl0[kQTile], sd0[kQTile];
+  __shared__ __attribute__((aligned(16))) float sl1[kQTile], sd1[kQTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, r32 = lane & 31;
@@ -131,14 +142,33 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dva[db][i] = dka[db][i] = 0.f;
 
-  TilePairStager<D, kQTile, kThreads> stage(tid);
-  float lse_r = 0.f, dl_r = 0.f;  // staged row statistics (threads < kQTile)
-  auto load_it = [&](int it) {
+  // Lane byte offsets of the LDS reads inside a Q or dO tile (swizzled like
+  // the forward's K/V tiles): 128-bit fragment reads per k-step and
+  // transposing reads per output column block; 32-row blocks and 16-row
+  // chunks add whole rows, which go into the instruction's offset field.
+  const int tr_row = 4 * hl + ((lane & 15) >> 2);
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  uint32_t foff[KS], troff[2][DB];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) foff[st] = 2 * tile_off<D>(r32, st * 16 + hl * 8);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      troff[h2][db] = 2 * tile_off<D>(tr_row + 8 * h2, db * 32 + tr_col);
+
+  // Q and dO tiles go straight into LDS (buffer loads with the LDS
+  // destination); the 64 row statistics of a tile go through registers.
+  const uint32_t qstride_b = (uint32_t)(qstride * 2);
+  const TileDma<D, kQTile, kThreads / 64> dma(wave, lane, qstride_b);
+  float lse_r = 0.f, dl_r = 0.f;  // row statistics of the next tile (threads < kQTile)
+  auto issue_it = [&](int it, __bf16* bq, __bf16* bdo) {
     const int gi = it / n_qt;
     const int i0 = q_lo + (it % n_qt) * kQTile;
     const int h = hkv * G + gi;
     const int64_t hoff = sp.q0 * qstride + (int64_t)h * D;
-    stage.load((const __bf16*)p.q + hoff, (const __bf16*)p.dout + hoff, qstride, i0, sp.lq);
+    dma.issue((const __bf16*)p.q + hoff, qstride_b, i0, sp.lq, bq);
+    dma.issue((const __bf16*)p.dout + hoff, qstride_b, i0, sp.lq, bdo);
     if (tid < kQTile) {
       const int i = i0 + tid;
       float l = kInf, dd = 0.f;
@@ -153,18 +183,9 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
     }
   };
 
-  int buf = 0;
-  if (n_it > 0) load_it(0);
-  for (int it = 0; it < n_it; ++it) {
+  auto compute = [&](int it, const __bf16* tq, const __bf16* tdo, const float* tl,
+                     const float* td) {
     const int i0 = q_lo + (it % n_qt) * kQTile;
-    stage.store(sq[buf], sdo[buf]);
-    if (tid < kQTile) {
-      slse[buf][tid] = lse_r;
-      sdl[buf][tid] = dl_r;
-    }
-    __syncthreads();
-    if (it + 1 < n_it) load_it(it + 1);
-
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qr0 = i0 + qb * 32;
@@ -184,9 +205,9 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const int off = tile_off<D>(qb * 32 + r32, st * 16 + hl * 8);
-        s = mfma32(as_bf16x8(lds_read_b128(sq[buf], off)), kf[st], s);
-        dp = mfma32(as_bf16x8(lds_read_b128(sdo[buf], off)), vf[st], dp);
+        const uint32_t ro = qb * 32 * D * 2;
+        s = mfma32(as_bf16x8(lds_read_b128_at(tq, foff[st], ro)), kf[st], s);
+        dp = mfma32(as_bf16x8(lds_read_b128_at(tdo, foff[st], ro)), vf[st], dp);
       }
 
       auto grads = [&](auto masked_tag) {
@@ -194,8 +215,8 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qrow = qb * 32 + 8 * r + 4 * hl;
-          const float4 L = *reinterpret_cast<const float4*>(&slse[buf][qrow]);
-          const float4 Dl = *reinterpret_cast<const float4*>(&sdl[buf][qrow]);
+          const float4 L = *reinterpret_cast<const float4*>(&tl[qrow]);
+          const float4 Dl = *reinterpret_cast<const float4*>(&td[qrow]);
           const float Lv[4] = {L.x, L.y, L.z, L.w};
           const float Dv[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
 #pragma unroll
@@ -216,8 +237,6 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 
       // dV^T += dO^T P and dK^T += Q^T dS over 16-query chunks; chunk qc
       // holds queries 16qc + 4hl + {0..3} and 16qc + 8 + 4hl + {0..3}
-      const int tr_row = qb * 32 + 4 * hl + ((lane & 15) >> 2);
-      const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
         const int j = qc * 8;
@@ -225,17 +244,38 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
                                       s[j + 5], s[j + 6], s[j + 7]);
         const bf16x8 dsb = pack_bf16x8(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
                                        dp[j + 5], dp[j + 6], dp[j + 7]);
+        const uint32_t ro = (qb * 32 + 16 * qc) * D * 2;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + tr_col;
-          const int o0 = tile_off<D>(16 * qc + tr_row, col);
-          const int o1 = tile_off<D>(16 * qc + 8 + tr_row, col);
-          dva[db] = mfma32(cat(lds_read_tr(sdo[buf], o0), lds_read_tr(sdo[buf], o1)), pb, dva[db]);
-          dka[db] = mfma32(cat(lds_read_tr(sq[buf], o0), lds_read_tr(sq[buf], o1)), dsb, dka[db]);
+          dva[db] = mfma32(cat(lds_read_tr_at(tdo, troff[0][db], ro),
+                               lds_read_tr_at(tdo, troff[1][db], ro)),
+                           pb, dva[db]);
+          dka[db] = mfma32(cat(lds_read_tr_at(tq, troff[0][db], ro),
+                               lds_read_tr_at(tq, troff[1][db], ro)),
+                           dsb, dka[db]);
         }
       }
     }
-    buf ^= 1;
+  };
+
+  // two buffers each, unrolled by two so that they are known at compile time
+  if (n_it > 0) issue_it(0, sq0, sdo0);
+  for (int it = 0; it < n_it; it += 2) {
+    if (tid < kQTile) {
+      sl0[tid] = lse_r;
+      sd0[tid] = dl_r;
+    }
+    dma_barrier();  // tile it is in buffer 0; buffer 1 is free
+    if (it + 1 < n_it) issue_it(it + 1, sq1, sdo1);
+    compute(it, sq0, sdo0, sl0, sd0);
+    if (it + 1 >= n_it) break;
+    if (tid < kQTile) {
+      sl1[tid] = lse_r;
+      sd1[tid] = dl_r;
+    }
+    dma_barrier();  // tile it + 1 is in buffer 1; buffer 0 is free
+    if (it + 2 < n_it) issue_it(it + 2, sq0, sdo0);
+    compute(it + 1, sq1, sdo1, sl1, sd1);
   }
 
   if (kj < sp.lk) {
@@ -260,13 +300,23 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 }
 
 // ------------------------------------------------------------ 3. dQ
+// Two waves per SIMD; the unmasked d = 128 instance does not fit their 256
+// registers without spilling and runs one wave per SIMD instead.
+template <int D, bool CAUSAL, bool WINDOW>
+constexpr int dq_waves_per_simd() { return (D == 128 && !CAUSAL && !WINDOW) ? 1 : 2; }
+
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<D, CAUSAL, WINDOW>())))
 void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   constexpr int KS = D / 16, DB = D / 32, NB = kKTile / 32, NC = kKTile / 16;
   constexpr float kInf = __builtin_inff();
-  __shared__ __attribute__((aligned(16))) __bf16 sk[2][kKTile * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sv[2][kKTile * D];
+  // two K/V buffers as distinct objects, so that reads of one buffer are not
+  // ordered behind the loads still landing in the other
+  __shared__ __attribute__((aligned(1024))) __bf16 sk0[kKTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sv0[kKTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sk1[kKTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sv1[kKTile * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, r32 = lane & 31;
@@ -324,73 +374,116 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 
   const int qlo_w = q_start + wave * 32;
   const int qhi_w = min(qlo_w + 31, sp.lq - 1);
-  TilePairStager<D, kKTile, kThreads> stage(tid);
-  int buf = 0;
-  if (kv_lo < kv_hi) stage.load(Kg, Vg, kstride, kv_lo, sp.lk);
-  for (int j0 = kv_lo; j0 < kv_hi; j0 += kKTile) {
-    stage.store(sk[buf], sv[buf]);
-    __syncthreads();
-    if (j0 + kKTile < kv_hi) stage.load(Kg, Vg, kstride, j0 + kKTile, sp.lk);
 
+  // Lane byte offsets of the LDS reads inside a K or V tile (same swizzled
+  // layout as the forward): 128-bit fragment reads per k-step, transposing
+  // reads of K per output column block; 32-row blocks and 16-row chunks add
+  // whole rows, which go into the instruction's offset field.
+  const int tr_row = 4 * hl + ((lane & 15) >> 2);
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  uint32_t foff[KS], troff[2][DB];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) foff[st] = 2 * tile_off<D>(r32, st * 16 + hl * 8);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      troff[h2][db] = 2 * tile_off<D>(tr_row + 8 * h2, db * 32 + tr_col);
+
+  // K and V tiles go straight from global memory into LDS (buffer loads with
+  // the LDS destination), two buffers each; the loads of tile j+1 are issued
+  // after the barrier that opens tile j.
+  const uint32_t kstride_b = (uint32_t)(kstride * 2);
+  const TileDma<D, kKTile, kThreads / 64> dma(wave, lane, kstride_b);
+  auto issue = [&](int j0, __bf16* kb, __bf16* vb) {
+    dma.issue(Kg, kstride_b, j0, sp.lk, kb);
+    dma.issue(Vg, kstride_b, j0, sp.lk, vb);
+  };
+  if (kv_lo < kv_hi) issue(kv_lo, sk0, sv0);
+
+  auto compute = [&](int j0, const __bf16* kt, const __bf16* vt) {
     bool active = qlo_w <= qhi_w;
     if (CAUSAL) active = active && (j0 <= qhi_w + delta);
     if (WINDOW) active = active && (j0 + kKTile - 1 > qlo_w + delta - p.window);
-    if (active) {
-      bool need_mask = (j0 + kKTile > sp.lk);
-      if (CAUSAL) need_mask = need_mask || (j0 + kKTile - 1 > qlo_w + delta);
-      if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
+    if (!active) return;
+    bool need_mask = (j0 + kKTile > sp.lk);
+    if (CAUSAL) need_mask = need_mask || (j0 + kKTile - 1 > qlo_w + delta);
+    if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
 
-      // S^T = K Q^T and dP^T = V dO^T: lane = query qi, rows = keys
-      f32x16 s[NB], dp[NB];
+    // One 32-key half kb of the tile at a time, to keep two score blocks
+    // live instead of four.  S^T = K Q^T and dP^T = V dO^T: lane = query
+    // qi, rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4.
+    auto half = [&](int kb, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      f32x16 s, dp;
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const int off = tile_off<D>(kb * 32 + r32, st * 16 + hl * 8);
-          s[kb] = mfma32(as_bf16x8(lds_read_b128(sk[buf], off)), qf[st], s[kb]);
-          dp[kb] = mfma32(as_bf16x8(lds_read_b128(sv[buf], off)), dof[st], dp[kb]);
-        }
+      for (int st = 0; st < KS; ++st) {
+        const uint32_t ro = kb * 32 * D * 2;
+        s = mfma32(as_bf16x8(lds_read_b128_at(kt, foff[st], ro)), qf[st], s);
+        dp = mfma32(as_bf16x8(lds_read_b128_at(vt, foff[st], ro)), dof[st], dp);
       }
-      auto grads = [&](auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
+      // a few fragment reads ahead of the MFMAs, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsAhead, 0);
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float pv = fast_exp2(fmaf(s[kb][i], c, -lse2));
-            if (MASKED) {
-              const int j = j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-              pv = visible<CAUSAL, WINDOW>(qi, j, delta, sp.lk, p.window) ? pv : 0.f;
-            }
-            dp[kb][i] = pv * (dp[kb][i] - dq_d);
-          }
-      };
-      if (need_mask)
-        grads(std::true_type{});
-      else
-        grads(std::false_type{});
+      for (int i = 0; i < 2 * KS - kReadsAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kReadsAhead, 0);
 
-      // dQ^T += K^T dS^T over 16-key chunks (same key permutation as the
-      // forward's P V product)
-      const int tr_row = 4 * hl + ((lane & 15) >> 2);
-      const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+      // P = exp2(S c - LSE log2 e), dS = P (dP - D); element i holds key
+      // base + off with off = 8(i/4) + i%4
+      const int base = j0 + kb * 32 + 4 * hl;
+      const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
 #pragma unroll
-      for (int kc = 0; kc < NC; ++kc) {
-        const int kb = kc >> 1, j = (kc & 1) * 8;
-        const bf16x8 dsb = pack_bf16x8(dp[kb][j], dp[kb][j + 1], dp[kb][j + 2], dp[kb][j + 3],
-                                       dp[kb][j + 4], dp[kb][j + 5], dp[kb][j + 6], dp[kb][j + 7]);
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(fmaf(s[i], c, -lse2));
+        if (MASKED) {
+          const int off = (i >> 2) * 8 + (i & 3);
+          bool ok = off < end;
+          if (CAUSAL) ok = ok && off <= hi;
+          if (WINDOW) ok = ok && off > lo;
+          pv = ok ? pv : 0.f;
+        }
+        dp[i] = pv * (dp[i] - dq_d);
+      }
+
+      // dQ^T += K^T dS^T over this half's two 16-key chunks (same key
+      // permutation as the forward's P V product)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int kc = 2 * kb + h2, j = h2 * 8;
+        const bf16x8 dsb = pack_bf16x8(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
+                                       dp[j + 5], dp[j + 6], dp[j + 7]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + tr_col;
-          const bf16x4 lo = lds_read_tr(sk[buf], tile_off<D>(16 * kc + tr_row, col));
-          const bf16x4 hi = lds_read_tr(sk[buf], tile_off<D>(16 * kc + 8 + tr_row, col));
-          acc[db] = mfma32(cat(lo, hi), dsb, acc[db]);
+          const uint32_t ro = 16 * kc * D * 2;
+          acc[db] = mfma32(cat(lds_read_tr_at(kt, troff[0][db], ro),
+                               lds_read_tr_at(kt, troff[1][db], ro)),
+                           dsb, acc[db]);
         }
       }
+    };
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      if (need_mask)
+        half(kb, std::true_type{});
+      else
+        half(kb, std::false_type{});
     }
-    buf ^= 1;
+  };
+
+#pragma nounroll
+  for (int j0 = kv_lo; j0 < kv_hi; j0 += 2 * kKTile) {
+    dma_barrier();  // tile j0 is in buffer 0; buffer 1 is free
+    if (j0 + kKTile < kv_hi) issue(j0 + kKTile, sk1, sv1);
+    compute(j0, sk0, sv0);
+    if (j0 + kKTile >= kv_hi) break;
+    dma_barrier();  // tile j0 + kKTile is in buffer 1; buffer 0 is free
+    if (j0 + 2 * kKTile < kv_hi) issue(j0 + 2 * kKTile, sk0, sv0);
+    compute(j0 + kKTile, sk1, sv1);
   }
 
   if (qi < sp.lq) {

@@ -84,26 +84,14 @@ __device__ __forceinline__ int tile_off(int r, int col) {
   return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
 }
 
-__device__ __forceinline__ uint4 lds_read_b128(const __bf16* base, int off) {
-  return *reinterpret_cast<const uint4*>(base + off);
-}
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address
-// of 4 consecutive bf16 (row j/4 of a 4-row block, columns 4*(j%4)..+3) and
-// receives column j of that 4 x 16 block (one element from each of the 4
-// rows).  Used to read V (or K, Q, dO) transposed for MFMA operands.
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* base, int off) {
-  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (FA_LDS i16x4*)(base + off));
-  return __builtin_bit_cast(bf16x4, t);
-}
-
-// The same two reads at a lane byte offset plus a byte offset that is a
-// compile-time constant after unrolling (whole rows, or a tile).  Keeping
-// the lane part in one register and the rest constant lets every read of a
-// tile reuse that register, with the constant in the instruction's offset
-// field; computing the full swizzled offset per read instead costs one
-// address register per distinct read.
+// LDS reads at a lane byte offset plus a byte offset that is a compile-time
+// constant after unrolling (whole rows, or a tile).  Keeping the lane part
+// in one register and the rest constant lets every read of a tile reuse that
+// register, with the constant in the instruction's offset field; computing
+// the full swizzled offset per read instead costs one address register per
+// distinct read.
+//
+// 128-bit read: one MFMA operand fragment (8 bf16 of one row) per lane.
 __device__ __forceinline__ uint4 lds_read_b128_at(const __bf16* base, uint32_t lane_off,
                                                   uint32_t const_off) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -111,6 +99,10 @@ __device__ __forceinline__ uint4 lds_read_b128_at(const __bf16* base, uint32_t l
                                          lane_off + const_off);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address
+// of 4 consecutive bf16 (row j/4 of a 4-row block, columns 4*(j%4)..+3) and
+// receives column j of that 4 x 16 block (one element from each of the 4
+// rows).  Used to read V (or K, Q, dO) transposed for MFMA operands.
 __device__ __forceinline__ bf16x4 lds_read_tr_at(const __bf16* base, uint32_t lane_off,
                                                  uint32_t const_off) {
   i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -124,46 +116,6 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
 }
-
-// Stages two [ROWS x D] bf16 tiles that share a row index (K and V, or Q and
-// dO) from global memory into swizzled LDS tiles, through registers so that
-// the global loads of the next tile can be in flight during compute.
-// Thread t covers 16-byte chunk t % (D/8) of rows t / (D/8) + pass * rows
-// per pass; rows at or past `limit` are written as zeros.
-template <int D, int ROWS, int THREADS>
-struct TilePairStager {
-  static constexpr int CPR = D / 8;
-  static constexpr int RPP = THREADS / CPR;
-  static constexpr int PASSES = ROWS / RPP;
-  static_assert(ROWS % RPP == 0, "tile rows must be a multiple of rows per pass");
-  uint4 a[PASSES], b[PASSES];
-  int c, r;
-  __device__ __forceinline__ explicit TilePairStager(int tid)
-      : c(tid % CPR), r(tid / CPR) {}
-  __device__ __forceinline__ void load(const __bf16* ga, const __bf16* gb,
-                                       int64_t stride, int j0, int limit) {
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int j = j0 + r + ps * RPP;
-      if (j < limit) {
-        a[ps] = *reinterpret_cast<const uint4*>(ga + j * stride + c * 8);
-        b[ps] = *reinterpret_cast<const uint4*>(gb + j * stride + c * 8);
-      } else {
-        a[ps] = make_uint4(0, 0, 0, 0);
-        b[ps] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* la, __bf16* lb) const {
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int row = r + ps * RPP;
-      const int off = row * D + ((c ^ swz<D>(row)) << 3);
-      *reinterpret_cast<uint4*>(la + off) = a[ps];
-      *reinterpret_cast<uint4*>(lb + off) = b[ps];
-    }
-  }
-};
 
 // ---------------------------------------------------------------- LDS DMA
 // Buffer loads that write straight into LDS (buffer_load_dwordx4 ... lds):
