@@ -66,7 +66,7 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 // and 4 aligned rows land in 4 distinct 64-byte groups.  D = 64 (8 chunks,
 // two rows per 256 bytes): same-parity rows of 16 map to distinct offsets.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ constexpr int swz(int r) {
   if constexpr (D == 128) {
     // bits 1..3 from r % 4 through the table {0, 6, 10, 12}, bit 0 = r/4 % 2,
     // bit 3 also flipped by r/8 % 2
@@ -80,7 +80,7 @@ __device__ __forceinline__ int swz(int r) {
 
 // Element offset of (row r, column col) in a swizzled tile with D columns.
 template <int D>
-__device__ __forceinline__ int tile_off(int r, int col) {
+__host__ __device__ constexpr int tile_off(int r, int col) {
   return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
 }
 
