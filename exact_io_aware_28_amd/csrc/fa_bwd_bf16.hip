@@ -97,8 +97,11 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
   uint32_t id = xcd_logical_id(blockIdx.x, gridDim.x);
   const int kt = id % num_ktiles;  // key tile 0 first: it sees the most rows
   id /= num_ktiles;
-  const int hkv = id % p.Hkv;
-  const int b = id / p.Hkv;
+  // the KV head is the slowest index, so each XCD's contiguous range holds
+  // whole KV heads (their query heads share the K/V in that XCD's L2) and
+  // every XCD sees the same mix of sequences (balanced for packed batches)
+  const int b = id % p.B;
+  const int hkv = id / p.B;
   const int G = p.group;
   const int32_t* cu = VARLEN ? p.cu_seqlens : nullptr;
   const SeqSpan sp = seq_span(cu, b, p.Nq, p.Nk);
@@ -327,8 +330,11 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   id /= G;
   const int t_ord = id % num_qtiles;
   id /= num_qtiles;
-  const int hkv = id % p.Hkv;
-  const int b = id / p.Hkv;
+  // the KV head is the slowest index, so each XCD's contiguous range holds
+  // whole KV heads (their query heads share the K/V in that XCD's L2) and
+  // every XCD sees the same mix of sequences (balanced for packed batches)
+  const int b = id % p.B;
+  const int hkv = id / p.B;
   const int h = hkv * G + gi;
   const int qt = CAUSAL ? (num_qtiles - 1 - t_ord) : t_ord;
   const int32_t* cu = VARLEN ? p.cu_seqlens : nullptr;

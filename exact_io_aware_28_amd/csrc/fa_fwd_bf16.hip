@@ -79,8 +79,11 @@ void fwd_bf16_kernel(FwdParams p) {
   id /= G;
   const int t_ord = id % p.num_qtiles;
   id /= p.num_qtiles;
-  const int hkv = id % p.Hkv;
-  const int b = id / p.Hkv;
+  // the KV head is the slowest index, so each XCD's contiguous range holds
+  // whole KV heads (their query heads share the K/V in that XCD's L2) and
+  // every XCD sees the same mix of sequences (balanced for packed batches)
+  const int b = id % p.B;
+  const int hkv = id / p.B;
   const int h = hkv * G + gi;
   // causal: longest rows first so that the tail of the grid is short
   const int qt = CAUSAL ? (p.num_qtiles - 1 - t_ord) : t_ord;
