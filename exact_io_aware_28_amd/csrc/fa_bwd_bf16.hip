@@ -42,30 +42,36 @@ constexpr int kKTile = 64;      // keys per staged tile in dQ
 constexpr int kReadsAhead = 4;  // LDS fragment reads issued ahead of the score MFMAs
 
 // ------------------------------------------------------------ 1. D = dO . O
+// D/8 consecutive lanes share one (token, head) row: each reads 16 contiguous
+// bytes of O and of dO, so a wave instruction covers whole rows, and the
+// partial dot products are summed with lane shuffles inside the group.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t token = idx / p.Hq;
-  const int h = (int)(idx % p.Hq);
-  int64_t out;
-  if (p.cu_seqlens) {
-    const int64_t T = p.cu_seqlens[p.B];
-    if (token >= T) return;
-    out = (int64_t)h * T + token;
-  } else {
-    if (token >= (int64_t)p.B * p.Nq) return;
-    const int64_t b = token / p.Nq, i = token % p.Nq;
-    out = (b * p.Hq + h) * p.Nq + i;
-  }
-  const int64_t base = (token * p.Hq + h) * D;
-  const uint4* o4 = reinterpret_cast<const uint4*>((const __bf16*)p.o + base);
-  const uint4* d4 = reinterpret_cast<const uint4*>((const __bf16*)p.dout + base);
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int part = threadIdx.x % kLanesPerRow;
+  const int64_t token = row / p.Hq;
+  const int h = (int)(row % p.Hq);
+  const int64_t T = p.cu_seqlens ? (int64_t)p.cu_seqlens[p.B] : (int64_t)p.B * p.Nq;
+  const bool valid = token < T;
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 a = as_bf16x8(o4[c]), g = as_bf16x8(d4[c]);
+  if (valid) {
+    const int64_t base = (token * p.Hq + h) * D + part * 8;
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>((const __bf16*)p.o + base));
+    const bf16x8 g = as_bf16x8(*reinterpret_cast<const uint4*>((const __bf16*)p.dout + base));
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int m = kLanesPerRow / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (!valid || part != 0) return;
+  int64_t out;
+  if (p.cu_seqlens) {
+    out = (int64_t)h * T + token;
+  } else {
+    const int64_t b = token / p.Nq, i = token % p.Nq;
+    out = (b * p.Hq + h) * p.Nq + i;
   }
   p.delta[out] = acc;
 }
@@ -527,8 +533,10 @@ hipError_t launch3(const BwdParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.Nq * p.Hq;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
+  const int64_t rows = (int64_t)p.B * p.Nq * p.Hq;  // >= tokens x heads, also when packed
+  const int64_t rows_per_block = kThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<D>),
+                     dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                      dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
