@@ -179,6 +179,56 @@ def time_backward(inp, dev, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def decode_pairs(inp):
+    """Visible (query row, key) pairs per head of a decode workload, summed
+    over sequences (bottom-right causal: row i sees i + L - Nq + 1 keys)."""
+    nq = inp["Nq"]
+    total = 0
+    for L in np.asarray(inp["seqlens_k"], dtype=np.int64):
+        for i in range(nq):
+            seen = L if not inp["causal"] else min(L, max(0, i + L - nq + 1))
+            if inp.get("window"):
+                seen = min(seen, inp["window"])
+            total += seen
+    return total
+
+
+def decode_bytes(inp):
+    """Algorithmic bytes of one decode call: the K/V rows in use read once,
+    Q read, O and LSE written (the split partials are not counted)."""
+    B, hq, hkv, nq, d = (inp[x] for x in ("B", "Hq", "Hkv", "Nq", "d"))
+    kv = int(np.asarray(inp["seqlens_k"], dtype=np.int64).sum()) * hkv * d * 2 * 2
+    return kv + 2 * B * nq * hq * d * 2 + B * hq * nq * 4
+
+
+def time_decode(inp, steps, warmup):
+    import torch
+    import exact_io_aware_28_amd as fa
+    q = torch.from_numpy(inp["q"]).to(torch.bfloat16).cuda()
+    k = torch.from_numpy(inp["k"]).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(inp["v"]).to(torch.bfloat16).cuda()
+    lens = torch.from_numpy(np.asarray(inp["seqlens_k"], np.int32)).cuda()
+    B, nq, hq, d = q.shape
+    splits = fa.fa_decode_num_splits(B, hq, k.shape[2], nq, k.shape[1])
+    ws = torch.empty(fa.fa_decode_workspace_size(B, hq, nq, d, splits), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, hq, nq), dtype=torch.float32, device="cuda")
+    kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"], seqlens_k=lens,
+              num_splits=splits, out=o, lse=lse, workspace=ws)
+    for _ in range(warmup + 1):
+        fa.fa_decode(q, k, v, **kw)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fa.fa_decode(q, k, v, **kw)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, splits
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size, for scaling the HBM
     counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
@@ -282,6 +332,16 @@ def main(argv=None):
                                   "TFLOP/s": round(2.5 * attention_flops(wi) / (bms * 1e-3) / 1e12, 2)}),
                       flush=True)
             del wd
+            torch.cuda.empty_cache()
+        for name in workloads.DECODE_WORKLOADS:
+            di = workloads.make_decode_inputs(name)
+            dms, splits = time_decode(di, max(a.steps, 10), a.warmup)
+            gbs = decode_bytes(di) / (dms * 1e-3) / 1e9
+            tf = 4.0 * di["Hq"] * di["d"] * decode_pairs(di) / (dms * 1e-3) / 1e12
+            print(json.dumps({"workload": name, "direction": "decode", "ms": round(dms, 4),
+                              "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                              "TFLOP/s": round(tf, 2), "num_splits": splits,
+                              "algorithmic_bytes": decode_bytes(di)}), flush=True)
             torch.cuda.empty_cache()
     return 0
 

@@ -10,6 +10,9 @@ Functions mirror the C ABI in include/fa_mi355x.h:
     fa_fwd_f32(...)  same, fp32 tensors
     fa_bwd(q, k, v, o, dout, lse, scale, ...) -> (dq, dk, dv)
     fa_bwd_workspace_size(T_q, Hq, d) -> int
+    fa_decode(q, k, v, scale, causal, window, seqlens_k, num_splits) -> (o, lse)
+    fa_decode_workspace_size(B, Hq, Nq, d, num_splits) -> int
+    fa_decode_num_splits(B, Hq, Hkv, Nq, Nk) -> int
     fa_status_string(status) -> str
 """
 
@@ -51,6 +54,13 @@ def lib():
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                              i, i, i, i, i, i, f, i, i, vp, vp]
         L.fa_bwd.restype = i
+        L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
+        L.fa_decode_workspace_size.restype = ctypes.c_size_t
+        L.fa_decode_num_splits.argtypes = [i, i, i, i, i]
+        L.fa_decode_num_splits.restype = i
+        L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, vp,
+                                ctypes.c_size_t, vp]
+        L.fa_decode.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -167,3 +177,40 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fa_decode_workspace_size(B, Hq, Nq, d, num_splits):
+    return int(lib().fa_decode_workspace_size(int(B), int(Hq), int(Nq), int(d),
+                                              int(num_splits)))
+
+
+def fa_decode_num_splits(B, Hq, Hkv, Nq, Nk):
+    return int(lib().fa_decode_num_splits(int(B), int(Hq), int(Hkv), int(Nq), int(Nk)))
+
+
+def fa_decode(q, k, v, scale=None, causal=False, window=0, seqlens_k=None,
+              num_splits=None, out=None, lse=None, workspace=None, stream=None):
+    """Split-KV attention of a few query rows per sequence over a K/V cache;
+    returns (o bf16 [B, Nq, Hq, d], lse fp32 [B, Hq, Nq])."""
+    import torch
+    _check({"q": q, "k": k, "v": v}, torch.bfloat16)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, None, None)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if seqlens_k is not None and seqlens_k.dtype != torch.int32:
+        raise TypeError("seqlens_k must be int32")
+    if num_splits is None:
+        num_splits = fa_decode_num_splits(B, hq, hkv, nq, nk)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
+    ws_bytes = fa_decode_workspace_size(B, hq, nq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv, nq,
+                         nk, d, float(scale), int(bool(causal)), int(window),
+                         _ptr(seqlens_k), int(num_splits), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode")
+    return out, lse

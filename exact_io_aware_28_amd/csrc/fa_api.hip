@@ -141,6 +141,75 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return fa::launch_bwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Split-KV workspace: normalised partial outputs [num_splits][B][Nq][Hq][d]
+// then partial LSEs [num_splits][B][Hq][Nq], both fp32, each part padded to
+// 256 bytes.
+static size_t decode_opart_bytes(int B, int Hq, int Nq, int d, int num_splits) {
+  const size_t n = (size_t)num_splits * B * Nq * Hq * d * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int Nq, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || Nq < 1 || d < 1 || num_splits < 1) return 0;
+  const size_t l = (size_t)num_splits * B * Hq * Nq * sizeof(float);
+  return decode_opart_bytes(B, Hq, Nq, d, num_splits) + ((l + 255) & ~(size_t)255);
+}
+
+int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0) return 0;
+  // enough single-wave work-groups to keep every CU streaming (about four
+  // per CU), without splitting below ~256 keys per split
+  const int64_t row_blocks = ((int64_t)(Hq / Hkv) * Nq + 31) / 32;
+  const int64_t base = (int64_t)B * Hkv * row_blocks;
+  int64_t s = (1024 + base - 1) / base;
+  const int64_t cap = Nk / 256 > 1 ? Nk / 256 : 1;
+  if (s > cap) s = cap;
+  if (s > 128) s = 128;
+  return (int)(s < 1 ? 1 : s);
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+              int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+              const int32_t* seqlens_k, int num_splits, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  const void* t[] = {q, k, v, o, workspace};
+  const float* s[] = {lse};
+  int st = check_common(t, 5, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window, nullptr,
+                        64);
+  if (st != FA_OK) return st;
+  if (seqlens_k && !aligned(seqlens_k, 4)) return FA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_decode_workspace_size(B, Hq, Nq, d, num_splits))
+    return FA_ERR_INVALID_ARG;
+  const int64_t row_blocks = ((int64_t)(Hq / Hkv) * Nq + 31) / 32;
+  if ((int64_t)num_splits * row_blocks * Hkv * B > (int64_t)UINT32_MAX / 2)
+    return FA_ERR_UNSUPPORTED;
+  fa::DecodeParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.seqlens_k = seqlens_k;
+  p.opart = static_cast<float*>(workspace);
+  p.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     decode_opart_bytes(B, Hq, Nq, d, num_splits));
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.group = Hq / Hkv;
+  p.causal = causal;
+  p.window = window;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.num_splits = num_splits;
+  p.row_blocks = (int)row_blocks;
+  return fa::launch_decode_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK:

@@ -164,16 +164,18 @@ void fwd_bf16_kernel(FwdParams p) {
     // S^T block kb: rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4, col = qi
     f32x16 s[NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      uint4 a[KS];
-#pragma unroll
-      for (int st = 0; st < KS; ++st)
-        a[st] = lds_read_b128_at(kt, koff[st], kb * 32 * D * 2);
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    // k-step outer, block inner: consecutive MFMAs accumulate into different
+    // blocks (measured ~0.5 % faster than two back-to-back chains)
 #pragma unroll
-      for (int st = 0; st < KS; ++st) s[kb] = mfma32(as_bf16x8(a[st]), qf[st], s[kb]);
-    }
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        const uint4 a = lds_read_b128_at(kt, koff[st], kb * 32 * D * 2);
+        s[kb] = mfma32(as_bf16x8(a), qf[st], s[kb]);
+      }
     // Schedule: issue kPrefetch K-fragment reads before the first MFMA, then
     // alternate one MFMA with one read, so several LDS reads stay in flight
     // while the matrix core works (the default schedule keeps about two).

@@ -44,9 +44,30 @@ struct BwdParams {
   float scale_log2;
 };
 
+// One split-KV call (few query rows per sequence over a long key cache),
+// already validated.  opart/lpart live in the caller's workspace.
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seqlens_k;   // keys used per sequence, or nullptr (all Nk)
+  float* opart;               // [num_splits][B][Nq][Hq][d] fp32, normalised partial O
+  float* lpart;               // [num_splits][B][Hq][Nq] fp32, partial LSE (natural log)
+  int B, Hq, Hkv, Nq, Nk, d;
+  int group;                  // Hq / Hkv
+  int causal, window;
+  float scale;
+  float scale_log2;
+  int num_splits;             // key-range splits per (sequence, KV head, row block)
+  int row_blocks;             // ceil(group * Nq / 32)
+};
+
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace fa

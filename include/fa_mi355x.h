@@ -137,6 +137,41 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            float scale, int causal, int window,
            const int32_t* cu_seqlens, void* stream);
 
+/*
+ * Split-KV attention for a few query rows per sequence over a long key/value
+ * cache: single-token decode and short chunked prefill, where the cost is
+ * streaming the cached keys and values (klaylearn.com glossary
+ * "flash-attention", "Does FlashAttention speed up every LLM inference
+ * path?").  Same result as fa_fwd on each sequence's first seqlens_k[b] keys:
+ * the key range is split over work-groups, each runs the online softmax over
+ * its range, and the partial results are merged exactly through their
+ * logsumexps (LSE = ln sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s).
+ *   q, o      : bf16 [B, Nq, Hq, d]
+ *   k, v      : bf16 [B, Nk, Hkv, d], a cache of capacity Nk per sequence
+ *   lse       : fp32 [B, Hq, Nq]
+ *   seqlens_k : NULL (every sequence uses all Nk keys) or device int32[B],
+ *               keys used by sequence b (clamped to [0, Nk]); query position
+ *               i of sequence b sits at key position i + seqlens_k[b] - Nq
+ *               for the causal and window masks (bottom-right alignment)
+ *   num_splits: 1..1024 key-range splits; fa_decode_num_splits gives a
+ *               default that fills the GPU
+ *   workspace : device buffer of at least
+ *               fa_decode_workspace_size(B, Hq, Nq, d, num_splits) bytes,
+ *               16-byte aligned, scratch for the partial results; it must
+ *               not alias any other argument
+ * Other arguments, mask conventions and errors as fa_fwd (no packed
+ * batches), plus FA_ERR_INVALID_ARG for num_splits out of range, a
+ * misaligned seqlens_k, or a NULL or too small workspace.  Costs O(Nk) per
+ * row; every K/V byte of a KV head is read once for its whole query group.
+ */
+size_t fa_decode_workspace_size(int B, int Hq, int Nq, int d, int num_splits);
+int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nq, int Nk, int d,
+              float scale, int causal, int window,
+              const int32_t* seqlens_k, int num_splits,
+              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(int status);
 

@@ -29,8 +29,9 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
-                                    "fa_fwd_f32", "fa_status_string"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode",
+                                    "fa_decode_num_splits", "fa_decode_workspace_size",
+                                    "fa_fwd", "fa_fwd_f32", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -131,6 +132,53 @@ def test_workspace_is_linear_in_rows():
     assert s1 >= 16384 * 16 * 4 and s2 <= 2 * s1 + 256
     assert fa.fa_bwd_workspace_size(0, 16, 128) == 0
     assert fa.fa_bwd_workspace_size(10, -1, 128) == 0
+
+
+def _dec(ws=P[9], ws_bytes=None, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, Hq=8, Hkv=2, Nq=1, Nk=4096,
+             d=128, scale=0.125, causal=1, window=0, lens=None, splits=4)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_decode_workspace_size(a["B"], a["Hq"], a["Nq"], a["d"],
+                                               max(a["splits"], 1))
+    return fa.lib().fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                              a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                              a["window"], a["lens"], a["splits"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(ws=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=64), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=1025), fa.FA_ERR_INVALID_ARG),
+    (dict(lens=ctypes.c_void_p(0x10002)), fa.FA_ERR_INVALID_ARG),  # misaligned
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=ctypes.c_void_p(0x20004)), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(window=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(bad, code):
+    assert _dec(**bad) == code
+
+
+def test_decode_workspace_and_default_splits():
+    # partial outputs (d floats) and partial LSEs (1 float) per split and row
+    s1 = fa.fa_decode_workspace_size(16, 32, 1, 128, 8)
+    assert 8 * 16 * 32 * 129 * 4 <= s1 <= 8 * 16 * 32 * 129 * 4 + 512
+    assert fa.fa_decode_workspace_size(16, 32, 1, 128, 0) == 0
+    assert fa.fa_decode_workspace_size(0, 32, 1, 128, 4) == 0
+    # enough work-groups to fill the chip, at least ~256 keys per split
+    assert fa.fa_decode_num_splits(16, 32, 8, 1, 8192) == 8
+    assert fa.fa_decode_num_splits(1, 32, 8, 1, 512) == 2
+    assert fa.fa_decode_num_splits(64, 32, 8, 1, 65536) == 2
+    assert fa.fa_decode_num_splits(1, 1, 1, 1, 100) == 1
+    assert 1 <= fa.fa_decode_num_splits(1, 8, 1, 1, 1 << 24) <= 128
+    assert fa.fa_decode_num_splits(1, 6, 4, 1, 100) == 0  # Hq % Hkv != 0
 
 
 def test_status_strings():

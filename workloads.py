@@ -11,7 +11,8 @@ bf16 values, so the GPU (after an exact cast to bf16) and the oracle (after an
 exact cast to fp64) see identical numbers.
 
 Draw order per workload: sequence lengths (packed batches only), then Q, K, V,
-then dO (workloads with a backward pass).
+then dO (workloads with a backward pass).  Decode workloads draw the cached
+key count of each sequence first, then Q, K, V.
 """
 
 import math
@@ -39,6 +40,16 @@ WORKLOADS = {
     # long causal forward + recomputation backward, B=2 H=16 N=16384 d=128
     "long_fwd_bwd": dict(B=2, Hq=16, Hkv=16, N=16384, d=128, dtype="bf16",
                          causal=True, window=0, seed=5, bwd=True),
+}
+
+
+# Decode over a key/value cache (few new query rows per sequence, long cache).
+#   kv_lengths: keys in use per sequence, drawn uniformly from [Lmin, Lmax]
+#   Nk: cache capacity per sequence (rows past a sequence's length are unused)
+DECODE_WORKLOADS = {
+    # single-token decode, 16 sequences, GQA 32/8, d=128, 1024..8192 cached keys
+    "decode_kv_cache": dict(B=16, Hq=32, Hkv=8, Nq=1, Nk=8192, d=128, Lmin=1024,
+                            Lmax=8192, causal=True, window=0, seed=6),
 }
 
 
@@ -113,4 +124,27 @@ def make_inputs(spec, seed=None, with_grad=None):
     out.setdefault("causal", False)
     out.setdefault("window", 0)
     out["dtype"] = dtype
+    return out
+
+
+def make_decode_inputs(spec, seed=None):
+    """Draw a decode workload: seqlens_k (int32 [B], drawn first), then q
+    [B, Nq, Hq, d], k and v [B, Nk, Hkv, d], all bf16-valued float32."""
+    if isinstance(spec, str):
+        spec = DECODE_WORKLOADS[spec]
+    spec = dict(spec)
+    seed = spec.get("seed", 0) if seed is None else seed
+    rng = np.random.default_rng(seed)
+    B, hq, hkv, nq, nk, d = (spec[x] for x in ("B", "Hq", "Hkv", "Nq", "Nk", "d"))
+    if "lengths" in spec:
+        lengths = np.asarray(spec["lengths"], dtype=np.int32)
+    else:
+        lengths = rng.integers(spec["Lmin"], spec["Lmax"] + 1, size=B).astype(np.int32)
+    out = dict(spec)
+    out["seqlens_k"] = lengths
+    out["q"] = _draw(rng, (B, nq, hq, d), "bf16")
+    out["k"] = _draw(rng, (B, nk, hkv, d), "bf16")
+    out["v"] = _draw(rng, (B, nk, hkv, d), "bf16")
+    out["scale"] = spec.get("scale", 1.0 / math.sqrt(d))
+    out["dtype"] = "bf16"
     return out
