@@ -31,7 +31,10 @@ constexpr int kDecThreads = 64;
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
 
 template <int D, bool CAUSAL, bool WINDOW>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams p) {
+// at most 256 registers, so that two waves share a SIMD: with 32 KB of LDS
+// per wave five fit a CU, and more tiles are in flight per CU
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeParams p) {
   constexpr int KS = D / 16;  // k-steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-column blocks of the output
   constexpr float kInf = __builtin_inff();

@@ -173,9 +173,9 @@ def test_decode_workspace_and_default_splits():
     assert fa.fa_decode_workspace_size(16, 32, 1, 128, 0) == 0
     assert fa.fa_decode_workspace_size(0, 32, 1, 128, 4) == 0
     # enough work-groups to fill the chip, at least ~256 keys per split
-    assert fa.fa_decode_num_splits(16, 32, 8, 1, 8192) == 8
+    assert fa.fa_decode_num_splits(16, 32, 8, 1, 8192) == 12
     assert fa.fa_decode_num_splits(1, 32, 8, 1, 512) == 2
-    assert fa.fa_decode_num_splits(64, 32, 8, 1, 65536) == 2
+    assert fa.fa_decode_num_splits(64, 32, 8, 1, 65536) == 3
     assert fa.fa_decode_num_splits(1, 1, 1, 1, 100) == 1
     assert 1 <= fa.fa_decode_num_splits(1, 8, 1, 1, 1 << 24) <= 128
     assert fa.fa_decode_num_splits(1, 6, 4, 1, 100) == 0  # Hq % Hkv != 0
