@@ -59,7 +59,7 @@ def attention_flops(inp):
 
 def algorithmic_bytes(inp):
     """Bytes the forward must move: Q, K, V read once, O and LSE written once."""
-    e = 2 if inp["dtype"] == "bf16" else 4
+    e = 4 if inp["dtype"] == "f32" else 2
     nq = inp["q"].size
     nk = inp["k"].size
     rows = inp["q"].shape[0] * (inp["q"].shape[1] if inp["q"].ndim == 4 else 1)
@@ -128,7 +128,7 @@ def cpu_baseline(inp, budget_s=12.0):
 
 def device_inputs(inp):
     import torch
-    dt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[inp["dtype"]]
     mk = lambda x: torch.from_numpy(x).to(dt).cuda()
     out = {n: mk(inp[n]) for n in ("q", "k", "v")}
     cu = inp.get("cu_seqlens")
@@ -139,7 +139,7 @@ def device_inputs(inp):
 def time_forward(inp, dev, steps, warmup):
     import torch
     import exact_io_aware_28_amd as fa
-    fn = fa.fa_fwd if inp["dtype"] == "bf16" else fa.fa_fwd_f32
+    fn = {"bf16": fa.fa_fwd, "f16": fa.fa_fwd_f16, "f32": fa.fa_fwd_f32}[inp["dtype"]]
     kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"],
               cu_seqlens=dev["cu"], max_seqlen=inp["Nq"] if dev["cu"] is not None else None)
     o, lse = fn(dev["q"], dev["k"], dev["v"], **kw)
@@ -333,6 +333,16 @@ def main(argv=None):
                       flush=True)
             del wd
             torch.cuda.empty_cache()
+        # the headline workload again with fp16 operands (same kernel body)
+        wi = workloads.make_inputs(dict(workloads.WORKLOADS[a.workload], dtype="f16"))
+        wd = device_inputs(wi)
+        wms = time_forward(wi, wd, a.steps, a.warmup)
+        print(json.dumps({"workload": a.workload, "direction": "fwd", "dtype": "f16",
+                          "ms": round(wms, 4),
+                          "TFLOP/s": round(attention_flops(wi) / (wms * 1e-3) / 1e12, 2)}),
+              flush=True)
+        del wd
+        torch.cuda.empty_cache()
         for name in workloads.DECODE_WORKLOADS:
             di = workloads.make_decode_inputs(name)
             dms, splits = time_decode(di, max(a.steps, 10), a.warmup)

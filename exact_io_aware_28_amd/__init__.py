@@ -7,6 +7,7 @@ import still succeeds but every call raises.
 
 Functions mirror the C ABI in include/fa_mi355x.h:
     fa_fwd(q, k, v, scale, causal, window, cu_seqlens, max_seqlen) -> (o, lse)
+    fa_fwd_f16(...)  same, fp16 tensors
     fa_fwd_f32(...)  same, fp32 tensors
     fa_bwd(q, k, v, o, dout, lse, scale, ...) -> (dq, dk, dv)
     fa_bwd_workspace_size(T_q, Hq, d) -> int
@@ -47,6 +48,8 @@ def lib():
         fwd_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, vp]
         L.fa_fwd.argtypes = fwd_args
         L.fa_fwd.restype = i
+        L.fa_fwd_f16.argtypes = fwd_args
+        L.fa_fwd_f16.restype = i
         L.fa_fwd_f32.argtypes = fwd_args
         L.fa_fwd_f32.restype = i
         L.fa_bwd_workspace_size.argtypes = [i, i, i]
@@ -142,6 +145,14 @@ def fa_fwd(q, k, v, scale=None, causal=False, window=0, cu_seqlens=None,
     """bf16 forward; returns (o bf16, lse fp32).  See include/fa_mi355x.h."""
     import torch
     return _fwd(lib().fa_fwd, torch.bfloat16, q, k, v, scale, causal, window,
+                cu_seqlens, max_seqlen, out, lse, stream)
+
+
+def fa_fwd_f16(q, k, v, scale=None, causal=False, window=0, cu_seqlens=None,
+               max_seqlen=None, out=None, lse=None, stream=None):
+    """fp16 forward; returns (o fp16, lse fp32)."""
+    import torch
+    return _fwd(lib().fa_fwd_f16, torch.float16, q, k, v, scale, causal, window,
                 cu_seqlens, max_seqlen, out, lse, stream)
 
 

@@ -83,6 +83,19 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return fa::launch_fwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+               const int32_t* cu_seqlens, void* stream) {
+  const void* t[] = {q, k, v, o};
+  const float* s[] = {lse};
+  int st = check_common(t, 4, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                        cu_seqlens, 64);
+  if (st != FA_OK) return st;
+  fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                               window, cu_seqlens);
+  return fa::launch_fwd_f16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
                const int32_t* cu_seqlens, void* stream) {

@@ -46,6 +46,48 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2,
   return r;
 }
 
+// The same operations for either 16-bit element type of the matrix
+// operands: bf16 (F16 = false) or IEEE fp16 (F16 = true,
+// v_mfma_f32_32x32x16_f16).  Operands move as raw 16-bit data in bf16x8
+// containers; only the MFMA, the rounding of fp32 values to 16 bits (nearest
+// even) and the element type of stores depend on the choice.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32_t(const bf16x8& a, const bf16x8& b,
+                                           const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ bf16x8 pack8_t(float a0, float a1, float a2, float a3, float a4,
+                                          float a5, float a6, float a7) {
+  if constexpr (F16) {
+    f16x8 r;
+    r[0] = (_Float16)a0; r[1] = (_Float16)a1; r[2] = (_Float16)a2; r[3] = (_Float16)a3;
+    r[4] = (_Float16)a4; r[5] = (_Float16)a5; r[6] = (_Float16)a6; r[7] = (_Float16)a7;
+    return __builtin_bit_cast(bf16x8, r);
+  } else {
+    return pack_bf16x8(a0, a1, a2, a3, a4, a5, a6, a7);
+  }
+}
+// Four fp32 values rounded to 16 bits, as the raw 8 bytes they are stored in
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <bool F16>
+__device__ __forceinline__ uint2 pack4_t(float a0, float a1, float a2, float a3) {
+  if constexpr (F16) {
+    f16x4 w;
+    w[0] = (_Float16)a0; w[1] = (_Float16)a1; w[2] = (_Float16)a2; w[3] = (_Float16)a3;
+    return __builtin_bit_cast(uint2, w);
+  } else {
+    bf16x4 w;
+    w[0] = (__bf16)a0; w[1] = (__bf16)a1; w[2] = (__bf16)a2; w[3] = (__bf16)a3;
+    return __builtin_bit_cast(uint2, w);
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }

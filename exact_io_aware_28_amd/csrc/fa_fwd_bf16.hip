@@ -49,7 +49,7 @@ namespace {
 constexpr int kBN = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
 
-template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN>
+template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int kWaves = W;
@@ -174,7 +174,7 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
         const uint4 a = lds_read_b128_at(kt, koff[st], kb * 32 * D * 2);
-        s[kb] = mfma32(as_bf16x8(a), qf[st], s[kb]);
+        s[kb] = mfma32_t<F16>(as_bf16x8(a), qf[st], s[kb]);
       }
     // Schedule: issue kPrefetch K-fragment reads before the first MFMA, then
     // alternate one MFMA with one read, so several LDS reads stay in flight
@@ -253,7 +253,7 @@ void fwd_bf16_kernel(FwdParams p) {
           else
             lsum0 += pv[e];
         }
-        const bf16x8 pb = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        const bf16x8 pb = pack8_t<F16>(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         bf16x8 va[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -261,7 +261,7 @@ void fwd_bf16_kernel(FwdParams p) {
                        lds_read_tr_at(vt, voff[1][db], 16 * kc * D * 2));
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = mfma32(va[db], pb, acc[db]);
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32_t<F16>(va[db], pb, acc[db]);
       }
       l_run += lsum0 + lsum1;
     };
@@ -291,13 +291,9 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        bf16x4 w;
-        w[0] = (__bf16)(acc[db][4 * r + 0] * inv);
-        w[1] = (__bf16)(acc[db][4 * r + 1] * inv);
-        w[2] = (__bf16)(acc[db][4 * r + 2] * inv);
-        w[3] = (__bf16)(acc[db][4 * r + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + r * 8 + hl * 4) =
-            __builtin_bit_cast(uint2, w);
+        const uint2 w = pack4_t<F16>(acc[db][4 * r + 0] * inv, acc[db][4 * r + 1] * inv,
+                                     acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv);
+        *reinterpret_cast<uint2*>(op + db * 32 + r * 8 + hl * 4) = w;
       }
     if (hl == 0) {
       const float m_sub = (m_run == -kInf) ? 0.f : m_run;
@@ -309,37 +305,42 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 // Launch with W waves per work-group; the query-tile count follows from W.
-template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN>
+template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16>
 hipError_t launch_w(FwdParams p, hipStream_t stream) {
   p.num_qtiles = (p.Nq + 32 * W - 1) / (32 * W);
   dim3 grid((unsigned)p.B * p.Hq * p.num_qtiles), block(64 * W);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, WINDOW, VARLEN>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, WINDOW, VARLEN, F16>), grid, block, 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, bool CAUSAL, bool WINDOW, bool F16>
 hipError_t launch3(const FwdParams& p, hipStream_t stream) {
   if constexpr (D == 128) {
-    if (p.cu_seqlens) return launch_w<D, 8, CAUSAL, WINDOW, true>(p, stream);
-    return launch_w<D, 8, CAUSAL, WINDOW, false>(p, stream);
+    if (p.cu_seqlens) return launch_w<D, 8, CAUSAL, WINDOW, true, F16>(p, stream);
+    return launch_w<D, 8, CAUSAL, WINDOW, false, F16>(p, stream);
   } else {
-    if (p.cu_seqlens) return launch_w<D, 4, CAUSAL, WINDOW, true>(p, stream);
-    return launch_w<D, 4, CAUSAL, WINDOW, false>(p, stream);
+    if (p.cu_seqlens) return launch_w<D, 4, CAUSAL, WINDOW, true, F16>(p, stream);
+    return launch_w<D, 4, CAUSAL, WINDOW, false, F16>(p, stream);
   }
 }
 
-template <int D>
+template <int D, bool F16>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   const bool win = p.window > 0;
   if (p.causal)
-    return win ? launch3<D, true, true>(p, stream) : launch3<D, true, false>(p, stream);
-  return win ? launch3<D, false, true>(p, stream) : launch3<D, false, false>(p, stream);
+    return win ? launch3<D, true, true, F16>(p, stream) : launch3<D, true, false, F16>(p, stream);
+  return win ? launch3<D, false, true, F16>(p, stream) : launch3<D, false, false, F16>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+  return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
+}
+
+hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream) {
+  return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
 }
 
 }  // namespace fa

@@ -96,6 +96,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* cu_seqlens, void* stream);
 
 /*
+ * Forward with IEEE fp16 q, k, v, o (same arguments, layouts and errors as
+ * fa_fwd; tokrepo.com "Flash Attention - Fast Memory-Efficient Exact
+ * Attention", "Self-Hosting & Configuration" names fp16 and bf16).  Scores,
+ * softmax state and the output accumulator are fp32; P is rounded to fp16
+ * (nearest even) for the P V product and O to fp16.
+ */
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               float scale, int causal, int window,
+               const int32_t* cu_seqlens, void* stream);
+
+/*
  * Forward with fp32 q, k, v, o (same arguments, layouts and errors as
  * fa_fwd, with 4 bytes per element).  Scores, softmax and the output
  * accumulator are computed in fp32 on the vector ALUs.

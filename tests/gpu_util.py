@@ -21,7 +21,7 @@ def say(*a):
 def to_dev(x, dtype="bf16"):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x))
-    t = t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)
+    t = t.to({"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype])
     return t.cuda()
 
 
@@ -30,14 +30,14 @@ def to_np(t):
 
 
 def run_fwd(inp):
-    """Call fa_fwd (or fa_fwd_f32) on a workloads.make_inputs() dict."""
+    """Call fa_fwd (fa_fwd_f16, fa_fwd_f32) on a workloads.make_inputs() dict."""
     import torch
     import exact_io_aware_28_amd as fa
     dt = inp.get("dtype", "bf16")
     q, k, v = (to_dev(inp[n], dt) for n in ("q", "k", "v"))
     cu = inp.get("cu_seqlens")
     cu_t = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).cuda()
-    fn = fa.fa_fwd if dt == "bf16" else fa.fa_fwd_f32
+    fn = {"bf16": fa.fa_fwd, "f16": fa.fa_fwd_f16, "f32": fa.fa_fwd_f32}[dt]
     o, lse = fn(q, k, v, scale=inp["scale"], causal=inp["causal"], window=inp["window"],
                 cu_seqlens=cu_t, max_seqlen=inp.get("Nq") if cu is not None else None)
     torch.cuda.synchronize()

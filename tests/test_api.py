@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode",
                                     "fa_decode_num_splits", "fa_decode_workspace_size",
-                                    "fa_fwd", "fa_fwd_f32", "fa_status_string"]
+                                    "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -92,7 +92,7 @@ BAD_FWD = [
 
 
 @pytest.mark.parametrize("bad,code", BAD_FWD)
-@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f16", "fa_fwd_f32"])
 def test_forward_rejects(entry, bad, code):
     assert _fwd(getattr(fa.lib(), entry), **bad) == code
 

@@ -228,3 +228,14 @@ def test_workload_shapes_and_determinism():
                                "seed": 7, "bwd": True})
     assert s["q"].shape == (1, 64, 4, 64) and s["do"].shape == (1, 64, 4, 64)
     assert np.array_equal(workloads.round_bf16(s["q"]), s["q"])
+
+
+def test_f16_inputs_are_exact_halves():
+    s = workloads.make_inputs({"B": 1, "Hq": 2, "Hkv": 1, "N": 100, "d": 64,
+                               "seed": 8, "dtype": "f16"})
+    for n in ("q", "k", "v"):
+        x = s[n]
+        assert x.dtype == np.float32
+        assert np.array_equal(x.astype(np.float16).astype(np.float32), x)
+        # not merely bf16 values: fp16 keeps bits that bf16 drops
+        assert not np.array_equal(workloads.round_bf16(x), x)

@@ -114,6 +114,33 @@ def test_fwd_f32_packed():
     assert np.abs(to_np(dev["o"]) - o_ref).max() < 1e-4
 
 
+# fp16 operands: P and O carry 11 significant bits instead of bf16's 8, so the
+# error sits well inside the bf16 bar; the tighter bound below would fail if
+# P or O were rounded to bf16 (and a bf16 reading of fp16 bits fails outright).
+F16_CASES = [
+    (2, 300, 300, 4, 2, 128, True, 0),
+    (1, 260, 260, 4, 4, 64, False, 0),
+    (1, 257, 257, 8, 1, 128, True, 0),        # MQA
+    (1, 500, 500, 4, 2, 128, True, 100),      # causal + window
+    (1, 100, 300, 4, 2, 64, True, 40),        # chunked prefill
+    (1, 300, 100, 4, 2, 128, True, 0),        # rows that see no key
+]
+
+
+@pytest.mark.parametrize("case", F16_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fwd_f16_small(case):
+    B, Nq, Nk, Hq, Hkv, d, causal, window = case
+    inp = _dense(B, Nq, Nk, Hq, Hkv, d, causal, window, seed=112, dtype="f16")
+    dev, o_ref, _ = _compare_full(inp, "f16 " + str(case))
+    assert np.abs(to_np(dev["o"]) - o_ref).max() < 3e-3
+
+
+def test_fwd_f16_packed():
+    inp = _packed(PACKED, 4, 2, 128, True, 50, seed=113, dtype="f16")
+    dev, o_ref, _ = _compare_full(inp, "f16 packed")
+    assert np.abs(to_np(dev["o"]) - o_ref).max() < 3e-3
+
+
 # ------------------------------------------------------------ properties
 def test_scale_zero_gives_counts():
     """scale = 0: LSE = ln(#visible keys) and O = mean of the visible V."""
@@ -261,6 +288,14 @@ def test_workload_gqa_causal_prefill():
     dev = run_fwd(inp)
     _sampled_heads_compare(inp, dev, {(0, 0), (0, 13)}, sample_rows(8192, count=64, seed=3),
                            "gqa_causal_prefill")
+
+
+def test_workload_gqa_causal_prefill_f16():
+    inp = workloads.make_inputs(dict(workloads.WORKLOADS["gqa_causal_prefill"], dtype="f16"))
+    say("[fwd] gqa_causal_prefill fp16 B=1 Hq=32 Hkv=8 N=8192 d=128 causal")
+    dev = run_fwd(inp)
+    _sampled_heads_compare(inp, dev, {(0, 21)}, sample_rows(8192, count=32, seed=4),
+                           "gqa_causal_prefill fp16")
 
 
 def test_workload_varlen_window():

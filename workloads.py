@@ -6,8 +6,8 @@ arithmetic, and neither the CPU oracle nor the HIP library depends on it.
 Every tensor is drawn i.i.d. N(0, 1) in float32 with numpy's PCG64
 (``numpy.random.default_rng(seed)``), in token-major layout with the head
 dimension innermost, then (for bf16 workloads) rounded to bfloat16 by
-round-to-nearest-even.  The arrays returned are float32 holding exactly the
-bf16 values, so the GPU (after an exact cast to bf16) and the oracle (after an
+round-to-nearest-even (fp16 workloads: to IEEE half, nearest even).  The
+arrays returned are float32 holding exactly the 16-bit values, so the GPU (after an exact cast to bf16) and the oracle (after an
 exact cast to fp64) see identical numbers.
 
 Draw order per workload: sequence lengths (packed batches only), then Q, K, V,
@@ -73,7 +73,11 @@ def round_bf16(x):
 
 def _draw(rng, shape, dtype):
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return round_bf16(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f16":  # IEEE half, nearest even (numpy's conversion)
+        return x.astype(np.float16).astype(np.float32)
+    return x
 
 
 def make_inputs(spec, seed=None, with_grad=None):
