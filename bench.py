@@ -63,7 +63,8 @@ def algorithmic_bytes(inp):
     nq = inp["q"].size
     nk = inp["k"].size
     rows = inp["q"].shape[0] * (inp["q"].shape[1] if inp["q"].ndim == 4 else 1)
-    return e * (2 * nq + 2 * nk) + 4 * rows * inp["Hq"]
+    bias = 0 if inp.get("bias") is None else inp["bias"].nbytes  # read once at least
+    return e * (2 * nq + 2 * nk) + 4 * rows * inp["Hq"] + bias
 
 
 def source_hash(names):
@@ -133,6 +134,7 @@ def device_inputs(inp):
     out = {n: mk(inp[n]) for n in ("q", "k", "v")}
     cu = inp.get("cu_seqlens")
     out["cu"] = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    out["bias"] = None if inp.get("bias") is None else torch.from_numpy(inp["bias"]).cuda()
     return out
 
 
@@ -142,6 +144,10 @@ def time_forward(inp, dev, steps, warmup):
     fn = {"bf16": fa.fa_fwd, "f16": fa.fa_fwd_f16, "f32": fa.fa_fwd_f32}[inp["dtype"]]
     kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"],
               cu_seqlens=dev["cu"], max_seqlen=inp["Nq"] if dev["cu"] is not None else None)
+    if dev.get("bias") is not None:  # same call with the bias in place of cu_seqlens
+        bias = dev["bias"]
+        kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"])
+        fn = lambda q, k, v, **a: fa.fa_fwd_bias(q, k, v, bias, **a)
     o, lse = fn(dev["q"], dev["k"], dev["v"], **kw)
     for _ in range(warmup):
         fn(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)
@@ -161,19 +167,25 @@ def time_backward(inp, dev, steps, warmup):
     import exact_io_aware_28_amd as fa
     kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"],
               cu_seqlens=dev["cu"], max_seqlen=inp["Nq"] if dev["cu"] is not None else None)
-    o, lse = fa.fa_fwd(dev["q"], dev["k"], dev["v"], **kw)
+    fwd, bwd = fa.fa_fwd, fa.fa_bwd
+    if dev.get("bias") is not None:
+        bias = dev["bias"]
+        kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"])
+        fwd = lambda q, k, v, **a: fa.fa_fwd_bias(q, k, v, bias, **a)
+        bwd = lambda q, k, v, o, do, lse, **a: fa.fa_bwd_bias(q, k, v, bias, o, do, lse, **a)
+    o, lse = fwd(dev["q"], dev["k"], dev["v"], **kw)
     do = torch.from_numpy(inp["do"]).to(torch.bfloat16).cuda()
-    dq, dk, dv = fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, do, lse, **kw)
+    dq, dk, dv = bwd(dev["q"], dev["k"], dev["v"], o, do, lse, **kw)
     ws = torch.empty(fa.fa_bwd_workspace_size(inp["B"] * inp["Nq"], inp["Hq"], inp["d"]),
                      dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
-        fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(steps):
-        fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
     stop.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps
@@ -324,7 +336,8 @@ def main(argv=None):
             wd = device_inputs(wi)
             wms = time_forward(wi, wd, max(a.steps, 10), a.warmup)
             extra = {"workload": name, "direction": "fwd", "ms": round(wms, 4),
-                     "TFLOP/s": round(attention_flops(wi) / (wms * 1e-3) / 1e12, 2)}
+                     "TFLOP/s": round(attention_flops(wi) / (wms * 1e-3) / 1e12, 2),
+                     "GB/s_algorithmic": round(algorithmic_bytes(wi) / (wms * 1e-3) / 1e9, 1)}
             print(json.dumps(extra), flush=True)
             if wi.get("bwd"):
                 bms = time_backward(wi, wd, 5, 1)

@@ -10,6 +10,8 @@ Functions mirror the C ABI in include/fa_mi355x.h:
     fa_fwd_f16(...)  same, fp16 tensors
     fa_fwd_f32(...)  same, fp32 tensors
     fa_bwd(q, k, v, o, dout, lse, scale, ...) -> (dq, dk, dv)
+    fa_fwd_bias(q, k, v, bias, scale, causal, window) -> (o, lse)
+    fa_bwd_bias(q, k, v, bias, o, dout, lse, scale, ...) -> (dq, dk, dv)
     fa_bwd_workspace_size(T_q, Hq, d) -> int
     fa_decode(q, k, v, scale, causal, window, seqlens_k, num_splits) -> (o, lse)
     fa_decode_workspace_size(B, Hq, Nq, d, num_splits) -> int
@@ -57,6 +59,13 @@ def lib():
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                              i, i, i, i, i, i, f, i, i, vp, vp]
         L.fa_bwd.restype = i
+        i64 = ctypes.c_int64
+        L.fa_fwd_bias.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
+                                  vp, i64, i64, i64, vp]
+        L.fa_fwd_bias.restype = i
+        L.fa_bwd_bias.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                  i, i, i, i, i, i, f, i, i, vp, i64, i64, i64, vp]
+        L.fa_bwd_bias.restype = i
         L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
         L.fa_decode_workspace_size.restype = ctypes.c_size_t
         L.fa_decode_num_splits.argtypes = [i, i, i, i, i]
@@ -187,6 +196,72 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
                       int(window), _ptr(cu_seqlens), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def _bias_view(bias, B, hq, nq, nk):
+    """(tensor, stride_b, stride_h, stride_q): an fp32 device bias that
+    broadcasts to [B, Hq, Nq, Nk] as a strided view (no copy unless its key
+    dimension is not contiguous)."""
+    import torch
+    if bias.dtype != torch.float32 or not bias.is_cuda:
+        raise TypeError("bias must be a float32 device tensor")
+    if bias.dim() > 4:
+        raise ValueError("bias must broadcast to [B, Hq, Nq, Nk]")
+    if bias.stride(-1) != 1 and bias.shape[-1] != 1:
+        bias = bias.contiguous()
+    if bias.shape[-1] == 1 and nk != 1:
+        raise ValueError("the key dimension of the bias cannot broadcast")
+    b4 = bias.reshape((1,) * (4 - bias.dim()) + tuple(bias.shape)) if bias.dim() < 4 else bias
+    e = b4.expand(B, hq, nq, nk)
+    return e, e.stride(0), e.stride(1), e.stride(2)
+
+
+def fa_fwd_bias(q, k, v, bias, scale=None, causal=False, window=0, out=None, lse=None,
+                stream=None):
+    """bf16 forward with an additive fp32 bias that broadcasts to
+    [B, Hq, Nq, Nk]; returns (o bf16, lse fp32).  Dense batches only."""
+    import torch
+    _check({"q": q, "k": k, "v": v}, torch.bfloat16)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, None, None)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
+    bt, sb, sh, sq = _bias_view(bias, B, hq, nq, nk)
+    st = lib().fa_fwd_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv, nq,
+                           nk, d, float(scale), int(bool(causal)), int(window), _ptr(bt),
+                           sb, sh, sq, _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_bias")
+    return out, lse
+
+
+def fa_bwd_bias(q, k, v, bias, o, dout, lse, scale=None, causal=False, window=0,
+                dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """bf16 backward of fa_fwd_bias (the bias is a constant); returns
+    (dq, dk, dv)."""
+    import torch
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, torch.bfloat16)
+    _check({"lse": lse}, torch.float32)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, None, None)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    bt, sb, sh, sq = _bias_view(bias, B, hq, nq, nk)
+    st = lib().fa_bwd_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(),
+                           B, hq, hkv, nq, nk, d, float(scale), int(bool(causal)),
+                           int(window), _ptr(bt), sb, sh, sq, _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_bias")
     return dq, dk, dv
 
 

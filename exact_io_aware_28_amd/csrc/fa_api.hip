@@ -63,7 +63,19 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.num_qtiles = 0;  // set by the launcher from its tile height
+  p.bias = nullptr;
+  p.bias_sb = p.bias_sh = p.bias_sq = 0;
+  p.bias_vec4 = 0;
   return p;
+}
+
+// An additive bias: non-null, 4-byte aligned, non-negative element strides.
+// Rows are read with 128-bit loads when every row start is 16-byte aligned.
+int check_bias(const float* bias, int64_t sb, int64_t sh, int64_t sq, int* vec4) {
+  if (!bias || !aligned(bias, 4)) return FA_ERR_INVALID_ARG;
+  if (sb < 0 || sh < 0 || sq < 0) return FA_ERR_INVALID_ARG;
+  *vec4 = aligned(bias, 16) && sb % 4 == 0 && sh % 4 == 0 && sq % 4 == 0;
+  return FA_OK;
 }
 
 }  // namespace
@@ -117,18 +129,52 @@ size_t fa_bwd_workspace_size(int T_q, int Hq, int d) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, void* workspace,
-           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-           int causal, int window, const int32_t* cu_seqlens, void* stream) {
+int fa_fwd_bias(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+                const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                int64_t bias_stride_q, void* stream) {
+  const void* t[] = {q, k, v, o};
+  const float* s[] = {lse};
+  int st = check_common(t, 4, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window, nullptr,
+                        64);
+  if (st != FA_OK) return st;
+  int vec4 = 0;
+  st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_q, &vec4);
+  if (st != FA_OK) return st;
+  fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                               window, nullptr);
+  p.bias = bias;
+  p.bias_sb = bias_stride_b;
+  p.bias_sh = bias_stride_h;
+  p.bias_sq = bias_stride_q;
+  p.bias_vec4 = vec4;
+  return fa::launch_fwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+static int bwd_impl(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                    int Nk, int d, float scale, int causal, int window,
+                    const int32_t* cu_seqlens, const float* bias, int64_t sb, int64_t sh,
+                    int64_t sq, int has_bias, void* stream) {
   const void* t[] = {q, k, v, o, dout, dq, dk, dv, workspace};
   const float* s[] = {lse};
   int st = check_common(t, 9, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
                         cu_seqlens, 64);
   if (st != FA_OK) return st;
+  int vec4 = 0;
+  if (has_bias) {
+    st = check_bias(bias, sb, sh, sq, &vec4);
+    if (st != FA_OK) return st;
+  }
   // packed batches: T <= B * Nq (each sequence is at most Nq long)
   if (workspace_bytes < fa_bwd_workspace_size(B * Nq, Hq, d)) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
+  p.bias = has_bias ? bias : nullptr;
+  p.bias_sb = sb;
+  p.bias_sh = sh;
+  p.bias_sq = sq;
+  p.bias_vec4 = vec4;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -152,6 +198,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   return fa::launch_bwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+           int causal, int window, const int32_t* cu_seqlens, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                  Nq, Nk, d, scale, causal, window, cu_seqlens, nullptr, 0, 0, 0, 0, stream);
+}
+
+int fa_bwd_bias(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                float scale, int causal, int window, const float* bias,
+                int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_q,
+                void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                  Nq, Nk, d, scale, causal, window, nullptr, bias, bias_stride_b,
+                  bias_stride_h, bias_stride_q, 1, stream);
 }
 
 // Split-KV workspace: normalised partial outputs [num_splits][B][Nq][Hq][d]

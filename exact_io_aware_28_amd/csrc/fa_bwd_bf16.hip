@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 template <int D>
 constexpr int dkdv_waves_per_simd() { return D == 64 ? 2 : 1; }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(dkdv_waves_per_simd<D>())))
 void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
@@ -207,6 +207,20 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
       if (CAUSAL) need_mask = need_mask || (qr0 + delta < kw_hi);
       if (WINDOW) need_mask = need_mask || (qr1 + delta - kw_lo >= p.window);
 
+      // bias at this lane's key for the block's 16 query rows (a column of
+      // the bias: consecutive lanes read consecutive keys), log2 units
+      float bv[BIAS ? 16 : 1];
+      if constexpr (BIAS) {
+        const int hb = hkv * G + it / n_qt;
+        const float* bcol = p.bias + (int64_t)b * p.bias_sb + (int64_t)hb * p.bias_sh +
+                            min(kj, sp.lk - 1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qr = qr0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+          bv[i] = (kj < sp.lk && qr < sp.lq) ? bcol[(int64_t)qr * p.bias_sq] * kLog2e : 0.f;
+        }
+      }
+
       // S = Q K^T and dP = dO V^T: lane = key kj, rows = queries
       // qb*32 + 8(i/4) + 4hl + i%4 of the staged tile
       f32x16 s, dp;
@@ -231,7 +245,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * r + e;
-            float pv = fast_exp2(fmaf(s[i], c, -Lv[e]));
+            float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - Lv[e] : -Lv[e]));
             if (MASKED)
               pv = visible<CAUSAL, WINDOW>(i0 + qrow + e, kj, delta, sp.lk, p.window) ? pv : 0.f;
             s[i] = pv;
@@ -309,14 +323,14 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 }
 
 // ------------------------------------------------------------ 3. dQ
-// Two waves per SIMD; the unmasked d = 128 instance does not fit their 256
-// registers without spilling and runs one wave per SIMD instead.
-template <int D, bool CAUSAL, bool WINDOW>
-constexpr int dq_waves_per_simd() { return (D == 128 && !CAUSAL && !WINDOW) ? 1 : 2; }
+// Two waves per SIMD; the unmasked and the biased d = 128 instances do not
+// fit their 256 registers without spilling and run one wave per SIMD instead.
+template <int D, bool CAUSAL, bool WINDOW, bool BIAS>
+constexpr int dq_waves_per_simd() { return (D == 128 && ((!CAUSAL && !WINDOW) || BIAS)) ? 1 : 2; }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<D, CAUSAL, WINDOW>())))
+__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<D, CAUSAL, WINDOW, BIAS>())))
 void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   constexpr int KS = D / 16, DB = D / 32, NB = kKTile / 32, NC = kKTile / 16;
   constexpr float kInf = __builtin_inff();
@@ -386,6 +400,10 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 
   const int qlo_w = q_start + wave * 32;
   const int qhi_w = min(qlo_w + 31, sp.lq - 1);
+  const float* brow = nullptr;  // this lane's bias row
+  if constexpr (BIAS)
+    brow = p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
+           (int64_t)min(qi, sp.lq - 1) * p.bias_sq;
 
   // Lane byte offsets of the LDS reads inside a K or V tile (same swizzled
   // layout as the forward): 128-bit fragment reads per k-step, transposing
@@ -427,6 +445,14 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
     // qi, rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4.
     auto half = [&](int kb, auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
+      // bias of this lane's row at keys j0 + 32kb + 8g + 4hl + {0..3}
+      float bv[BIAS ? 16 : 1];
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          bias4_log2(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq,
+                     p.bias_vec4 != 0, &bv[4 * g]);
+      }
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
@@ -451,7 +477,7 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(s[i], c, -lse2));
+        float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - lse2 : -lse2));
         if (MASKED) {
           const int off = (i >> 2) * 8 + (i & 3);
           bool ok = off < end;
@@ -512,21 +538,22 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   }
 }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false>
 hipError_t launch4(const BwdParams& p, hipStream_t stream) {
   const int nkt = (p.Nk + kKeyBlock - 1) / kKeyBlock;
   const int nqt = (p.Nq + kQBlock - 1) / kQBlock;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS>),
                      dim3((unsigned)p.B * p.Hkv * nkt), dim3(kThreads), 0, stream, p, nkt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WINDOW, VARLEN>),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS>),
                      dim3((unsigned)p.B * p.Hq * nqt), dim3(kThreads), 0, stream, p, nqt);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch3(const BwdParams& p, hipStream_t stream) {
+  if (p.bias) return launch4<D, CAUSAL, WINDOW, false, true>(p, stream);  // dense only
   return p.cu_seqlens ? launch4<D, CAUSAL, WINDOW, true>(p, stream)
                       : launch4<D, CAUSAL, WINDOW, false>(p, stream);
 }

@@ -31,6 +31,9 @@
 //     Rows past the sequence end read as zeros (descriptor bounds check).
 //   * Causal and window masks skip whole tiles; element masks are only
 //     evaluated on tiles that straddle a boundary.
+//   * An optional additive bias (a custom mask, -inf hiding a key) is read
+//     from global memory per tile and folded into the scores in log2 units
+//     before the row maximum, so the rest of the update is unchanged.
 //   * Lazy rescaling: the running maximum used for exponentiation is only
 //     raised when a row's maximum grows by more than 2^8, so most tiles skip
 //     the accumulator rescale.  Scores stay <= 2^8 in fp32, and O and LSE
@@ -49,8 +52,15 @@ namespace {
 constexpr int kBN = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
 
-template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+// Waves per SIMD: two, except with a bias at d = 128 (four waves per group,
+// one per SIMD), where the bias values of a tile do not fit the 256
+// registers that two waves leave each.
+template <int D, bool BIAS>
+constexpr int fwd_waves_per_simd() { return (BIAS && D == 128) ? 1 : 2; }
+
+template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BIAS>
+__global__ __launch_bounds__(64 * W)
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd<D, BIAS>())))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int kWaves = W;
   constexpr int kBM = 32 * kWaves;      // query rows per work-group
@@ -132,6 +142,13 @@ void fwd_bf16_kernel(FwdParams p) {
   float m_run = -kInf;  // reference maximum, scaled (log2) units
   float l_run = 0.f;    // this half-wave's share of the normaliser
   const float c = p.scale_log2;
+  // with a bias the scores are turned into log2 units right after the
+  // product, and the softmax update below multiplies by 1
+  const float cs = BIAS ? 1.0f : c;
+  const float* brow = nullptr;  // this lane's bias row
+  if constexpr (BIAS)
+    brow = p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
+           (int64_t)min(qi, sp.lq - 1) * p.bias_sq;
 
   const int qlo_w = q_start + wave * 32;
   const int qhi_w = min(qlo_w + 31, sp.lq - 1);
@@ -161,6 +178,18 @@ void fwd_bf16_kernel(FwdParams p) {
     if (CAUSAL) need_mask = need_mask || (j0 + kBN - 1 > qlo_w + delta);
     if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
 
+    // bias of this lane's row at the keys its score elements hold; the
+    // loads are issued before the products and land while they run
+    float bv[BIAS ? NB : 1][16];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          bias4_log2(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq,
+                     p.bias_vec4 != 0, &bv[kb][4 * g]);
+    }
+
     // S^T block kb: rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4, col = qi
     f32x16 s[NB];
 #pragma unroll
@@ -186,13 +215,19 @@ void fwd_bf16_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(s[kb][i], c, bv[kb][i]);
+    }
 
     // Online-softmax update and P V product.  MASKED tiles straddle a mask
     // boundary: an invisible score is replaced by a sentinel that never wins
     // the row extreme, and its probability is forced to zero.
     auto softmax_tile = [&](auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      const float sentinel = (c >= 0.f) ? -kInf : kInf;
+      const float sentinel = (cs >= 0.f) ? -kInf : kInf;
       auto key_of = [&](int kb, int i) { return j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3); };
       if (MASKED) {
 #pragma unroll
@@ -204,7 +239,7 @@ void fwd_bf16_kernel(FwdParams p) {
       }
       // row extreme of the raw scores (max for c >= 0, min for c < 0)
       float rm = s[0][0];
-      if (c >= 0.f) {
+      if (cs >= 0.f) {
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -217,7 +252,7 @@ void fwd_bf16_kernel(FwdParams p) {
           for (int i = 0; i < 16; ++i) rm = fminf(rm, s[kb][i]);
         rm = fminf(rm, xor32(rm));
       }
-      const float tmax = __builtin_isinf(rm) ? -kInf : rm * c;
+      const float tmax = __builtin_isinf(rm) ? -kInf : rm * cs;
 
       float m_use = m_run;
       if (tmax > m_run + kRescaleSlack) m_use = tmax;  // also when m_run = -inf
@@ -244,7 +279,7 @@ void fwd_bf16_kernel(FwdParams p) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(s[kb][i0 + e], c, neg));
+          pv[e] = fast_exp2(fmaf(s[kb][i0 + e], cs, neg));
           if (MASKED)
             pv[e] = visible<CAUSAL, WINDOW>(qi, key_of(kb, i0 + e), delta, sp.lk, p.window)
                         ? pv[e] : 0.f;
@@ -305,17 +340,20 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 // Launch with W waves per work-group; the query-tile count follows from W.
-template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16>
+template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BIAS = false>
 hipError_t launch_w(FwdParams p, hipStream_t stream) {
   p.num_qtiles = (p.Nq + 32 * W - 1) / (32 * W);
   dim3 grid((unsigned)p.B * p.Hq * p.num_qtiles), block(64 * W);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, WINDOW, VARLEN, F16>), grid, block, 0,
-                     stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, WINDOW, VARLEN, F16, BIAS>), grid, block,
+                     0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool WINDOW, bool F16>
 hipError_t launch3(const FwdParams& p, hipStream_t stream) {
+  if constexpr (!F16) {  // bias: bf16, dense batches
+    if (p.bias) return launch_w<D, 4, CAUSAL, WINDOW, false, false, true>(p, stream);
+  }
   if constexpr (D == 128) {
     if (p.cu_seqlens) return launch_w<D, 8, CAUSAL, WINDOW, true, F16>(p, stream);
     return launch_w<D, 8, CAUSAL, WINDOW, false, F16>(p, stream);

@@ -23,6 +23,11 @@ struct FwdParams {
   float scale;                // multiplier of Q K^T
   float scale_log2;           // scale * log2(e): exp(x*scale) = exp2(x*scale_log2)
   int num_qtiles;             // ceil(Nq / query-tile rows) of the kernel
+  // additive bias of dense batches, nullptr when there is none: element
+  // (b, h, i, j) at bias[b*bias_sb + h*bias_sh + i*bias_sq + j]
+  const float* bias;
+  int64_t bias_sb, bias_sh, bias_sq;
+  int bias_vec4;              // every row start is 16-byte aligned
 };
 
 struct BwdParams {
@@ -42,6 +47,9 @@ struct BwdParams {
   int causal, window;
   float scale;
   float scale_log2;
+  const float* bias;          // as in FwdParams
+  int64_t bias_sb, bias_sh, bias_sq;
+  int bias_vec4;
 };
 
 // One split-KV call (few query rows per sequence over a long key cache),

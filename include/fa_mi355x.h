@@ -150,6 +150,40 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const int32_t* cu_seqlens, void* stream);
 
 /*
+ * Forward and backward with an additive bias (a custom attention mask:
+ * tokrepo.com "Flash Attention - Fast Memory-Efficient Exact Attention",
+ * "Key Features"):  S = scale * Q K^T + bias, then the causal and window
+ * masks as in fa_fwd, then the same softmax, O and LSE.  A -inf entry hides
+ * a key; a row whose every visible key is hidden gets O = 0, LSE = -inf.
+ * The bias is a constant: fa_bwd_bias returns dQ, dK, dV only.  Dense
+ * batches only (no cu_seqlens); other arguments, layouts and errors as
+ * fa_fwd and fa_bwd.
+ *   bias : fp32, caller-owned device memory; element (b, h, i, j) for batch
+ *          entry b, query head h, query row i, key j is
+ *          bias[b*bias_stride_b + h*bias_stride_h + i*bias_stride_q + j]
+ *          and must be readable for every b < B, h < Hq, i < Nq, j < Nk.
+ *          A stride of 0 broadcasts (e.g. one [Nq, Nk] bias for all heads,
+ *          or a key-padding row with bias_stride_q = 0).
+ *   bias_stride_* : element strides, >= 0
+ * Returns FA_ERR_INVALID_ARG, in addition to fa_fwd's cases, for a NULL or
+ * not 4-byte-aligned bias or a negative stride.  Rows are read 16 bytes at a
+ * time when the bias is 16-byte aligned and every stride is a multiple of 4,
+ * element by element otherwise (slower).  Entries must be finite or -inf.
+ */
+int fa_fwd_bias(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                float scale, int causal, int window,
+                const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                int64_t bias_stride_q, void* stream);
+int fa_bwd_bias(const void* q, const void* k, const void* v, const void* o,
+                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes,
+                int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                float scale, int causal, int window,
+                const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                int64_t bias_stride_q, void* stream);
+
+/*
  * Split-KV attention for a few query rows per sequence over a long key/value
  * cache: single-token decode and short chunked prefill, where the cost is
  * streaming the cached keys and values (klaylearn.com glossary

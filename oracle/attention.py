@@ -26,7 +26,12 @@ Definitions used:
           (i + Nk - Nq) - j < W;  W <= 0 means no window;
         - query head h reads KV head h // (Hq / Hkv) (contiguous groups);
         - in a packed batch a query only sees keys of its own sequence;
-        - a row with no visible key has O = 0 and LSE = -inf.
+        - a row with no visible key has O = 0 and LSE = -inf;
+        - a custom mask ([tok] "Key Features" lists custom attention masks)
+          is an additive bias B added to the scaled scores before the
+          softmax, S = scale * Q K^T + B, with -inf entries hiding a key;
+          it is a constant of the problem, so it has no gradient here, and
+          it combines with the causal and window masks.
   * the saved row statistic is the natural-log logsumexp
       LSE_i = m_i + ln(l_i) = ln(sum_j exp(S_ij))
       ([tok] "Architecture Overview" names logsumexp; [llms] "3. Recomputation
@@ -93,9 +98,13 @@ def _softmax_rows(s):
     return p, lse
 
 
-def _head_fwd(q, k, v, scale, ok):
-    """One (sequence, head): q [nq,d], k/v [nk,d] fp64 -> O, LSE, P."""
+def _head_fwd(q, k, v, scale, ok, bias=None):
+    """One (sequence, head): q [nq,d], k/v [nk,d] fp64 -> O, LSE, P.
+
+    bias: None or [nq, nk], added to the scaled scores."""
     s = scale * (q @ k.T)
+    if bias is not None:
+        s = s + np.asarray(bias, np.float64)
     s = np.where(ok, s, -np.inf)
     p, lse = _softmax_rows(s)
     return p @ v, lse, p
@@ -115,9 +124,21 @@ def _as_packed(x):
     return x.reshape(-1, x.shape[-2], x.shape[-1]) if x.ndim == 4 else x
 
 
-def attn_fwd(q, k, v, scale, causal=False, window=0, cu_seqlens=None):
-    """Exact attention forward.  Returns (O, LSE) in the module's layouts."""
+def _bias_of(bias, B, hq, nq, nk):
+    """The bias as a read-only [B, Hq, Nq, Nk] view (numpy broadcasting)."""
+    if bias is None:
+        return None
+    return np.broadcast_to(bias, (B, hq, nq, nk))
+
+
+def attn_fwd(q, k, v, scale, causal=False, window=0, cu_seqlens=None, bias=None):
+    """Exact attention forward.  Returns (O, LSE) in the module's layouts.
+
+    bias: None, or (dense batches only) an array that broadcasts to
+    [B, Hq, Nq, Nk], added to the scaled scores."""
     dense = cu_seqlens is None
+    if bias is not None and not dense:
+        raise ValueError("a bias is defined for dense batches only")
     if dense:
         B, nq, hq, d = q.shape
         nk, hkv = k.shape[1], k.shape[2]
@@ -132,6 +153,7 @@ def attn_fwd(q, k, v, scale, causal=False, window=0, cu_seqlens=None):
     else:
         lse = np.full((hq, qp.shape[0]), -np.inf)
         qspans = kspans = sequence_spans(None, None, cu_seqlens)
+    bb = _bias_of(bias, B, hq, nq, nk) if dense else None
     for s, ((q0, lq), (k0, lk)) in enumerate(zip(qspans, kspans)):
         if lq == 0:
             continue
@@ -139,7 +161,8 @@ def attn_fwd(q, k, v, scale, causal=False, window=0, cu_seqlens=None):
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             oh, lh, _ = _head_fwd(qp[q0:q0 + lq, h], kp[k0:k0 + lk, g],
-                                  vp[k0:k0 + lk, g], scale, ok)
+                                  vp[k0:k0 + lk, g], scale, ok,
+                                  None if bb is None else bb[s, h])
             o[q0:q0 + lq, h] = oh
             if dense:
                 lse[s, h] = lh
@@ -157,25 +180,26 @@ def probabilities(q, k, scale, causal=False, window=0):
     return _softmax_rows(s)[0]
 
 
-def attn_fwd_rows(q_h, k_g, v_g, rows, scale, causal=False, window=0):
+def attn_fwd_rows(q_h, k_g, v_g, rows, scale, causal=False, window=0, bias=None):
     """O and LSE of selected query rows of one (sequence, head).
 
-    q_h [nq,d], k_g/v_g [nk,d]; rows: indices into q_h.  Each row is the
-    plain definition over the whole key row, so any subset of rows can be
-    checked at any sequence length.
+    q_h [nq,d], k_g/v_g [nk,d]; rows: indices into q_h; bias: None or this
+    head's [nq, nk] bias.  Each row is the plain definition over the whole
+    key row, so any subset of rows can be checked at any sequence length.
     """
     q_h = np.asarray(q_h, np.float64)
     k_g = np.asarray(k_g, np.float64)
     v_g = np.asarray(v_g, np.float64)
     rows = np.asarray(rows, dtype=np.int64)
     ok = _rows_allowed(rows, len(q_h), len(k_g), causal, window)
-    o, lse, _ = _head_fwd(q_h[rows], k_g, v_g, scale, ok)
+    o, lse, _ = _head_fwd(q_h[rows], k_g, v_g, scale, ok,
+                          None if bias is None else np.asarray(bias)[rows])
     return o, lse
 
 
-def _head_bwd(q, k, v, do, scale, ok):
+def _head_bwd(q, k, v, do, scale, ok, bias=None):
     """One (sequence, head) backward from the definition: returns dq, dk, dv."""
-    o, _, p = _head_fwd(q, k, v, scale, ok)
+    o, _, p = _head_fwd(q, k, v, scale, ok, bias)
     dv = p.T @ do
     dp = do @ v.T
     dvec = (do * o).sum(axis=1)
@@ -185,9 +209,12 @@ def _head_bwd(q, k, v, do, scale, ok):
     return dq, dk, dv
 
 
-def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None):
-    """Exact gradients (dQ, dK, dV) of sum(O * dO), same layouts as Q, K, V."""
+def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None, bias=None):
+    """Exact gradients (dQ, dK, dV) of sum(O * dO), same layouts as Q, K, V
+    (bias as in attn_fwd, held constant)."""
     dense = cu_seqlens is None
+    if bias is not None and not dense:
+        raise ValueError("a bias is defined for dense batches only")
     if dense:
         B, nq, hq, d = q.shape
         nk, hkv = k.shape[1], k.shape[2]
@@ -200,14 +227,16 @@ def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None):
     dq = np.zeros(qp.shape)
     dk = np.zeros(kp.shape)
     dv = np.zeros(vp.shape)
-    for (q0, lq), (k0, lk) in zip(qspans, kspans):
+    bb = _bias_of(bias, B, hq, nq, nk) if dense else None
+    for s, ((q0, lq), (k0, lk)) in enumerate(zip(qspans, kspans)):
         if lq == 0:
             continue
         ok = allowed_mask(lq, lk, causal, window)
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             a, b, c = _head_bwd(qp[q0:q0 + lq, h], kp[k0:k0 + lk, g],
-                                vp[k0:k0 + lk, g], dop[q0:q0 + lq, h], scale, ok)
+                                vp[k0:k0 + lk, g], dop[q0:q0 + lq, h], scale, ok,
+                                None if bb is None else bb[s, h])
             dq[q0:q0 + lq, h] = a
             dk[k0:k0 + lk, g] += b
             dv[k0:k0 + lk, g] += c
@@ -215,13 +244,13 @@ def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None):
 
 
 def attn_bwd_sampled(q, k, v, do, scale, causal, window, b, g, q_rows, k_rows,
-                     chunk=2048):
+                     chunk=2048, bias=None):
     """Gradients of one dense batch entry b and KV head g, at sampled rows.
 
     Returns (dq [len(q_rows), G, d] for the G query heads of KV head g,
              dk [len(k_rows), d], dv [len(k_rows), d]).
 
-    Same definitions as attn_bwd; the full rows of P are rebuilt chunk by
+    Same definitions as attn_bwd (bias as there); the full rows of P are rebuilt chunk by
     chunk of query rows (each chunk a full-row softmax, no running state) so
     that long sequences fit in host memory.
     """
@@ -236,13 +265,16 @@ def attn_bwd_sampled(q, k, v, do, scale, causal, window, b, g, q_rows, k_rows,
     dq = np.zeros((len(q_rows), G, d))
     dk = np.zeros((len(k_rows), d))
     dv = np.zeros((len(k_rows), d))
+    bb = _bias_of(bias, q.shape[0], hq, nq, nk)
     for gi in range(G):
         h = g * G + gi
         qh = np.asarray(q[b, :, h], np.float64)
         doh = np.asarray(do[b, :, h], np.float64)
+        bh = None if bb is None else bb[b, h]
         # dQ rows: each needs only its own full row of P and dP.
         ok = _rows_allowed(q_rows, nq, nk, causal, window)
-        o_r, _, p_r = _head_fwd(qh[q_rows], kb, vb, scale, ok)
+        o_r, _, p_r = _head_fwd(qh[q_rows], kb, vb, scale, ok,
+                                None if bh is None else bh[q_rows])
         dp_r = doh[q_rows] @ vb.T
         dvec_r = (doh[q_rows] * o_r).sum(axis=1)
         dq[:, gi] = scale * ((p_r * (dp_r - dvec_r[:, None])) @ kb)
@@ -250,7 +282,8 @@ def attn_bwd_sampled(q, k, v, do, scale, causal, window, b, g, q_rows, k_rows,
         for c0 in range(0, nq, chunk):
             rows = np.arange(c0, min(nq, c0 + chunk))
             okc = _rows_allowed(rows, nq, nk, causal, window)
-            o_c, _, p_c = _head_fwd(qh[rows], kb, vb, scale, okc)
+            o_c, _, p_c = _head_fwd(qh[rows], kb, vb, scale, okc,
+                                    None if bh is None else bh[rows])
             dvec_c = (doh[rows] * o_c).sum(axis=1)
             pj = p_c[:, k_rows]
             dpj = doh[rows] @ vb[k_rows].T

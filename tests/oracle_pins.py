@@ -352,12 +352,142 @@ def check_empty_rows(A):
     assert np.all(np.isfinite(o[0, 2:])) and np.all(np.isfinite(lse[0, 0, 2:]))
 
 
+# ------------------------------------------------ additive mask / bias
+def _torch_sdpa_bias(q, k, v, scale, mask):
+    """torch float64 SDPA with a float attn_mask added to the scaled scores."""
+    G = q.shape[2] // k.shape[2]
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.from_numpy(np.array(mask)), scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def _random_bias(rng, shape, frac_masked=0.2):
+    b = rng.standard_normal(shape) * 2.0
+    b[rng.random(shape) < frac_masked] = -np.inf
+    b[..., 0] = np.where(np.isinf(b[..., 0]), 0.5, b[..., 0])  # every row keeps a key
+    return b
+
+
+def check_bias_against_torch_sdpa(A):
+    """Bias of several broadcast shapes, with -inf entries, against torch SDPA
+    with the same float attn_mask (plus the causal mask written out)."""
+    rng = _rng(40)
+    for B, nq, nk, hq, hkv, d in [(2, 19, 27, 4, 2, 8), (1, 15, 15, 2, 1, 8)]:
+        _bias_vs_torch(A, rng, B, nq, nk, hq, hkv, d)
+
+
+def _bias_vs_torch(A, rng, B, nq, nk, hq, hkv, d):
+    q, k, v = _dense(rng, B, nq, nk, hq, hkv, d)
+    for shape in [(B, hq, nq, nk), (B, 1, nq, nk), (1, hq, 1, nk), (nq, nk)]:
+        bias = _random_bias(rng, shape)
+        o, _ = A.attn_fwd(q, k, v, 0.4, bias=bias)
+        full = np.broadcast_to(bias, (B, hq, nq, nk))
+        assert np.allclose(o, _torch_sdpa_bias(q, k, v, 0.4, full), atol=1e-12)
+        # causal on top: torch gets the lower-right triangle as -inf entries
+        o, _ = A.attn_fwd(q, k, v, 0.4, causal=True, bias=bias)
+        j = np.arange(nk)[None, :]
+        i = np.arange(nq)[:, None] + (nk - nq)
+        both = np.where(j <= i, full, -np.inf)
+        assert np.allclose(o, _torch_sdpa_bias(q, k, v, 0.4, both), atol=1e-12)
+
+
+def check_bias_row_constant(A):
+    """A bias constant along each row leaves O alone and adds it to LSE
+    (softmax is invariant to a per-row shift)."""
+    rng = _rng(41)
+    q, k, v = _dense(rng, 1, 13, 21, 2, 1, 8)
+    c = rng.standard_normal((1, 2, 13, 1)) * 3.0
+    for causal, window in [(False, 0), (True, 5)]:
+        o1, l1 = A.attn_fwd(q, k, v, 0.6, causal, window)
+        o2, l2 = A.attn_fwd(q, k, v, 0.6, causal, window, bias=c)
+        assert np.allclose(o1, o2, atol=1e-12)
+        assert np.allclose(l2, l1 + c[..., 0], atol=1e-12)
+
+
+def check_bias_is_key_shift(A):
+    """bias = scale Q W^T gives exactly attention with keys K + W (the bias is
+    added to the scaled score of query i and key j); dK and dV agree too."""
+    rng = _rng(42)
+    B, nq, nk, hq, d = 1, 11, 17, 2, 6
+    q, k, v = _dense(rng, B, nq, nk, hq, hq, d)
+    w = rng.standard_normal(k.shape)
+    do = rng.standard_normal(q.shape)
+    bias = 0.7 * np.einsum("bihd,bjhd->bhij", q, w)
+    for causal in (False, True):
+        o1, l1 = A.attn_fwd(q, k + w, v, 0.7, causal)
+        o2, l2 = A.attn_fwd(q, k, v, 0.7, causal, bias=bias)
+        assert np.allclose(o1, o2, atol=1e-11) and np.allclose(l1, l2, atol=1e-11)
+        _, dk1, dv1 = A.attn_bwd(q, k + w, v, do, 0.7, causal)
+        _, dk2, dv2 = A.attn_bwd(q, k, v, do, 0.7, causal, bias=bias)
+        assert np.allclose(dk1, dk2, atol=1e-11) and np.allclose(dv1, dv2, atol=1e-11)
+
+
+def check_bias_mask_equals_causal(A):
+    """A {0, -inf} bias shaped like the causal mask equals causal=True, and a
+    row that the bias hides completely gives O = 0 and LSE = -inf."""
+    rng = _rng(43)
+    q, k, v = _dense(rng, 1, 9, 14, 2, 2, 8)
+    j = np.arange(14)[None, :]
+    i = np.arange(9)[:, None] + 5
+    m = np.where(j <= i, 0.0, -np.inf)
+    o1, l1 = A.attn_fwd(q, k, v, 0.5, causal=True)
+    o2, l2 = A.attn_fwd(q, k, v, 0.5, bias=m)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    m2 = np.zeros((9, 14))
+    m2[3] = -np.inf
+    o3, l3 = A.attn_fwd(q, k, v, 0.5, bias=m2)
+    assert np.all(o3[0, 3] == 0) and np.all(np.isneginf(l3[0, :, 3]))
+    assert np.all(np.isfinite(np.delete(o3[0], 3, axis=0)))
+
+
+def check_bias_backward_autograd(A):
+    """Gradients with a constant float mask against torch autograd through
+    float64 SDPA, and central finite differences on a tiny case."""
+    rng = _rng(44)
+    q, k, v = _dense(rng, 2, 12, 16, 4, 2, 8)
+    do = rng.standard_normal(q.shape)
+    bias = _random_bias(rng, (2, 1, 12, 16))
+    dq, dk, dv = A.attn_bwd(q, k, v, do, 0.45, bias=bias)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.permute(0, 2, 1, 3), tk.permute(0, 2, 1, 3).repeat_interleave(2, dim=1),
+        tv.permute(0, 2, 1, 3).repeat_interleave(2, dim=1),
+        attn_mask=torch.from_numpy(np.array(np.broadcast_to(bias, (2, 4, 12, 16)))),
+        scale=0.45).permute(0, 2, 1, 3)
+    (o * torch.from_numpy(do)).sum().backward()
+    assert np.allclose(dq, tq.grad.numpy(), atol=1e-11)
+    assert np.allclose(dk, tk.grad.numpy(), atol=1e-11)
+    assert np.allclose(dv, tv.grad.numpy(), atol=1e-11)
+    # finite differences, bias with a window on top
+    q, k, v = _dense(rng, 1, 5, 7, 1, 1, 3)
+    do = rng.standard_normal(q.shape)
+    bias = _random_bias(rng, (5, 7))
+    dq, dk, dv = A.attn_bwd(q, k, v, do, 0.8, True, 4, bias=bias)
+    loss = lambda: float((A.attn_fwd(q, k, v, 0.8, True, 4, bias=bias)[0] * do).sum())
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x[idx] += h
+            fp = loss()
+            x[idx] -= 2 * h
+            fm = loss()
+            x[idx] += h
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.abs(num - g).max() <= 1e-6 * max(np.abs(num).max(), 1e-30)
+
+
 ALL_FORWARD = [check_rows_sum_to_one, check_identical_keys, check_dominant_score,
                check_permutation_invariance, check_lse_is_logsumexp,
                check_scale_zero, check_against_torch_sdpa, check_brute_force_tiny,
                check_hand_worked_golden, check_gqa_is_repeated_mha,
                check_varlen_is_concatenation, check_key_translation,
                check_causal_row_zero, check_chunked_prefill_alignment,
-               check_empty_rows]
+               check_empty_rows, check_bias_against_torch_sdpa,
+               check_bias_row_constant, check_bias_is_key_shift,
+               check_bias_mask_equals_causal]
 ALL_BACKWARD = [check_backward_finite_differences, check_backward_autograd,
-                check_backward_invariants]
+                check_backward_invariants, check_bias_backward_autograd]

@@ -29,9 +29,10 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode",
-                                    "fa_decode_num_splits", "fa_decode_workspace_size",
-                                    "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_status_string"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_workspace_size",
+                                    "fa_decode", "fa_decode_num_splits",
+                                    "fa_decode_workspace_size", "fa_fwd", "fa_fwd_bias",
+                                    "fa_fwd_f16", "fa_fwd_f32", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -179,6 +180,47 @@ def test_decode_workspace_and_default_splits():
     assert fa.fa_decode_num_splits(1, 1, 1, 1, 100) == 1
     assert 1 <= fa.fa_decode_num_splits(1, 8, 1, 1, 1 << 24) <= 128
     assert fa.fa_decode_num_splits(1, 6, 4, 1, 100) == 0  # Hq % Hkv != 0
+
+
+def _fwd_bias(bias=P[6], sb=0, sh=0, sq=64, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, Hq=4, Hkv=2, Nq=64, Nk=64,
+             d=128, scale=0.125, causal=0, window=0)
+    a.update(kw)
+    return fa.lib().fa_fwd_bias(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                a["window"], bias, sb, sh, sq, None)
+
+
+def _bwd_bias(bias=P[10], sb=0, sh=0, sq=64, ws_bytes=None, **kw):
+    a = dict(B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125, causal=0, window=0)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_size(a["B"] * a["Nq"], a["Hq"], a["d"])
+    return fa.lib().fa_bwd_bias(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9],
+                                ws_bytes, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                a["scale"], a["causal"], a["window"], bias, sb, sh, sq, None)
+
+
+BAD_BIAS = [
+    (dict(bias=None), fa.FA_ERR_INVALID_ARG),
+    (dict(bias=ctypes.c_void_p(0x70002)), fa.FA_ERR_INVALID_ARG),  # not 4-byte aligned
+    (dict(sb=-4), fa.FA_ERR_INVALID_ARG),
+    (dict(sh=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(sq=-64), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=5), fa.FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("bad,code", BAD_BIAS)
+def test_bias_entry_points_reject(bad, code):
+    assert _fwd_bias(**bad) == code
+    assert _bwd_bias(**{k: v for k, v in bad.items()}) == code
+
+
+def test_bias_backward_checks_workspace():
+    assert _bwd_bias(ws_bytes=8) == fa.FA_ERR_INVALID_ARG
 
 
 def test_status_strings():

@@ -1,0 +1,162 @@
+"""GPU parity of the additive-bias path (fa_fwd_bias, fa_bwd_bias) against
+the fp64 oracle.
+
+The bias is fp32 and added to the scaled scores before the causal/window
+masks and the softmax; -inf entries hide keys.  Cases cover every broadcast
+the strides allow (per head, shared by the heads, a key-padding row shared by
+the query rows, a strided view), the 128-bit and the element-wise read paths
+(row strides that are and are not multiples of 4 floats), ragged tiles,
+chunked prefill (Nq < Nk), rows that the bias hides completely (O = 0,
+LSE = -inf, zero gradients), d = 64 and 128, MQA, and the full biased
+8192-token workload on sampled rows.  Tolerances as the unbiased path
+(tests/gpu_util.py).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import check_grad, check_lse, check_o, say, sample_rows, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_28_amd as fa
+    fa.lib()  # fail loudly if the library is missing
+
+
+def _inputs(B, Nq, Nk, Hq, Hkv, d, causal, window, shape, seed, masked=0.15):
+    inp = workloads.make_inputs(dict(B=B, Nq=Nq, Nk=Nk, Hq=Hq, Hkv=Hkv, d=d, causal=causal,
+                                     window=window, seed=seed, bwd=True, bias_shape=shape,
+                                     bias_masked=masked))
+    return inp
+
+
+def _bias_dev(bias, pad=0):
+    """The bias on the device; pad > 0 stores it as a view of a wider tensor
+    (row stride Nk + pad)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bias))
+    if pad:
+        wide = torch.full(t.shape[:-1] + (t.shape[-1] + pad,), 7.0, dtype=torch.float32)
+        wide[..., :t.shape[-1]] = t
+        return wide.cuda()[..., :t.shape[-1]]
+    return t.cuda()
+
+
+def _run(inp, pad=0, bwd=True):
+    import torch
+    import exact_io_aware_28_amd as fa
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    bias = _bias_dev(inp["bias"], pad)
+    o, lse = fa.fa_fwd_bias(q, k, v, bias, scale=inp["scale"], causal=inp["causal"],
+                            window=inp["window"])
+    grads = None
+    if bwd:
+        grads = fa.fa_bwd_bias(q, k, v, bias, o, do, lse, scale=inp["scale"],
+                               causal=inp["causal"], window=inp["window"])
+    torch.cuda.synchronize()
+    return o, lse, grads
+
+
+def _check_full(inp, what, pad=0, bwd=True):
+    say(f"[bias] {what}")
+    o, lse, grads = _run(inp, pad, bwd)
+    f = lambda n: inp[n].astype(np.float64)
+    o_ref, lse_ref = oracle.attn_fwd(f("q"), f("k"), f("v"), inp["scale"], inp["causal"],
+                                     inp["window"], bias=inp["bias"])
+    check_o(to_np(o), o_ref, what)
+    check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, what)
+    if bwd:
+        ref = oracle.attn_bwd(f("q"), f("k"), f("v"), f("do"), inp["scale"], inp["causal"],
+                              inp["window"], bias=inp["bias"])
+        for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+            check_grad(to_np(g), r, f"{what} {name}")
+    return o, lse, grads
+
+
+CASES = [
+    # B, Nq, Nk, Hq, Hkv, d, causal, window, bias shape, row padding
+    (2, 300, 300, 4, 2, 128, False, 0, ("B", "H", "Q", "K"), 0),   # per head, 128-bit reads
+    (2, 257, 257, 4, 2, 64, True, 0, ("B", 1, "Q", "K"), 0),       # row stride 257: element reads
+    (2, 200, 200, 4, 2, 128, True, 60, ("B", 1, 1, "K"), 0),       # key padding row, window
+    (1, 100, 300, 4, 2, 128, True, 0, (1, "H", "Q", "K"), 0),      # chunked prefill
+    (1, 190, 190, 8, 1, 128, False, 0, (1, 1, "Q", "K"), 3),       # MQA, strided view
+    (1, 130, 130, 2, 2, 64, False, 0, (1, 1, "Q", "K"), 2),        # strided, 16-byte rows
+    (1, 64, 64, 2, 1, 128, True, 0, (1, 1, "Q", "K"), 0),          # exact tile
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_bias_small(case):
+    B, Nq, Nk, Hq, Hkv, d, causal, window, shape, pad = case
+    inp = _inputs(B, Nq, Nk, Hq, Hkv, d, causal, window, shape, seed=200 + Nq)
+    _check_full(inp, f"B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} "
+                     f"window={window} bias={shape} pad={pad}", pad=pad)
+
+
+def test_bias_hidden_rows():
+    """Rows whose every key the bias hides: O = 0, LSE = -inf, and their
+    gradients vanish; the other rows are unaffected."""
+    inp = _inputs(1, 150, 150, 2, 1, 128, False, 0, (1, 1, "Q", "K"), seed=230)
+    inp["bias"][0, 0, [0, 77, 149]] = -np.inf
+    o, lse, (dq, dk, dv) = _check_full(inp, "hidden rows")
+    o, lse, dq = to_np(o), lse.cpu().numpy(), to_np(dq)
+    for r in (0, 77, 149):
+        assert np.all(o[0, r] == 0) and np.all(np.isneginf(lse[0, :, r]))
+        assert np.all(dq[0, r] == 0)
+
+
+def test_bias_zero_equals_unbiased():
+    """An all-zero bias gives the unbiased forward (same bits up to the fp32
+    order of the scale and log2(e) products)."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    inp = _inputs(1, 400, 400, 4, 2, 128, True, 0, (1, 1, "Q", "K"), seed=231)
+    inp["bias"][:] = 0.0
+    o1, l1, _ = _run(inp, bwd=False)
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    o2, l2 = fa.fa_fwd(q, k, v, scale=inp["scale"], causal=True)
+    torch.cuda.synchronize()
+    assert np.abs(to_np(o1) - to_np(o2)).max() <= 8e-3
+    assert np.abs(l1.cpu().numpy() - l2.cpu().numpy()).max() <= 1e-5
+
+
+def test_bias_workload_sampled():
+    """The biased GQA workload (B=1, Hq=32, Hkv=8, N=8192, d=128, one shared
+    fp32 [N, N] bias with 10 % -inf entries) in the launch configuration the
+    bench times: forward on sampled rows of every head plus one whole head,
+    backward on sampled rows of one KV group."""
+    inp = workloads.make_inputs("gqa_bias")
+    say("[bias] gqa_bias B=1 Hq=32 Hkv=8 N=8192 d=128 shared [N, N] bias")
+    o, lse, (dq, dk, dv) = _run(inp)
+    o, lse = to_np(o), lse.cpu().numpy().astype(np.float64)
+    bias = inp["bias"][0, 0]
+    rows = sample_rows(8192, count=24, seed=7)
+    outs, refs, lerr = [], [], 0.0
+    for h in range(32):
+        g = h // 4
+        rr = np.arange(8192) if h == 5 else rows
+        ro, rl = oracle.attn_fwd_rows(inp["q"][0, :, h], inp["k"][0, :, g], inp["v"][0, :, g],
+                                      rr, inp["scale"], False, 0, bias=bias)
+        outs.append(o[0, rr, h])
+        refs.append(ro)
+        lerr = max(lerr, float(np.abs(lse[0, h, rr] - rl).max()))
+    check_o(np.concatenate(outs), np.concatenate(refs), "gqa_bias fwd")
+    say(f"  gqa_bias LSE max|err|={lerr:.3e}")
+    assert lerr <= 1e-3
+    dq, dk, dv = to_np(dq), to_np(dk), to_np(dv)
+    qr = sample_rows(8192, count=16, seed=1)
+    kr = sample_rows(8192, count=16, seed=2)
+    g = 6
+    rq, rk, rv = oracle.attn_bwd_sampled(inp["q"], inp["k"], inp["v"], inp["do"], inp["scale"],
+                                         False, 0, 0, g, qr, kr, chunk=2048, bias=inp["bias"])
+    check_grad(dq[0][qr][:, 4 * g:4 * g + 4], rq, "gqa_bias dQ")
+    check_grad(dk[0, kr, g], rk, "gqa_bias dK")
+    check_grad(dv[0, kr, g], rv, "gqa_bias dV")

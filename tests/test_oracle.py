@@ -80,27 +80,58 @@ def _lse_without_max(s):
     return p, lse - np.where(np.isfinite(m), m, 0.0)
 
 
-def _head_fwd_no_scale(q, k, v, scale, ok):
-    s = np.where(ok, q @ k.T, -np.inf)
+def _head_fwd_no_scale(q, k, v, scale, ok, bias=None):
+    s = q @ k.T + (0.0 if bias is None else bias)
+    s = np.where(ok, s, -np.inf)
     p, lse = A._softmax_rows(s)
     return p @ v, lse, p
 
 
-def _head_bwd_missing_D(q, k, v, do, scale, ok):
-    o, _, p = A._head_fwd(q, k, v, scale, ok)
+def _head_bwd_missing_D(q, k, v, do, scale, ok, bias=None):
+    o, _, p = A._head_fwd(q, k, v, scale, ok, bias)
     ds = p * (do @ v.T)
     return scale * (ds @ k), scale * (ds.T @ q), p.T @ do
 
 
-def _head_bwd_unscaled_dk(q, k, v, do, scale, ok):
-    dq, dk, dv = A._head_bwd(q, k, v, do, scale, ok)
+def _head_bwd_unscaled_dk(q, k, v, do, scale, ok, bias=None):
+    dq, dk, dv = A._head_bwd(q, k, v, do, scale, ok, bias)
     return dq, dk / scale, dv
 
 
-def _head_bwd_transposed_dv(q, k, v, do, scale, ok):
-    dq, dk, _ = A._head_bwd(q, k, v, do, scale, ok)
-    _, _, p = A._head_fwd(q, k, v, scale, ok)
+def _head_bwd_transposed_dv(q, k, v, do, scale, ok, bias=None):
+    dq, dk, _ = A._head_bwd(q, k, v, do, scale, ok, bias)
+    _, _, p = A._head_fwd(q, k, v, scale, ok, bias)
     return dq, dk, p @ do  # P instead of P^T (the pins use square shapes)
+
+
+def _head_fwd_bias_scaled(q, k, v, scale, ok, bias=None):
+    s = scale * (q @ k.T + (0.0 if bias is None else bias))
+    p, lse = A._softmax_rows(np.where(ok, s, -np.inf))
+    return p @ v, lse, p
+
+
+def _head_fwd_bias_subtracted(q, k, v, scale, ok, bias=None):
+    s = scale * (q @ k.T) - (0.0 if bias is None else bias)
+    p, lse = A._softmax_rows(np.where(ok, s, -np.inf))
+    return p @ v, lse, p
+
+
+def _head_fwd_bias_transposed(q, k, v, scale, ok, bias=None):
+    b = 0.0 if bias is None else np.asarray(bias)
+    if np.ndim(b) == 2 and b.shape[0] == b.shape[1]:
+        b = b.T
+    p, lse = A._softmax_rows(np.where(ok, scale * (q @ k.T) + b, -np.inf))
+    return p @ v, lse, p
+
+
+def _head_bwd_bias_dropped(q, k, v, do, scale, ok, bias=None):
+    return A._head_bwd(q, k, v, do, scale, ok, None)
+
+
+def _bias_of_head_swapped(bias, B, hq, nq, nk):
+    if bias is None:
+        return None
+    return np.broadcast_to(bias, (B, hq, nq, nk))[:, ::-1]
 
 
 MUTATIONS = {
@@ -113,6 +144,11 @@ MUTATIONS = {
     "bwd_missing_D": dict(_head_bwd=_head_bwd_missing_D),
     "bwd_dk_unscaled": dict(_head_bwd=_head_bwd_unscaled_dk),
     "bwd_dv_transposed": dict(_head_bwd=_head_bwd_transposed_dv),
+    "bias_scaled_with_scores": dict(_head_fwd=_head_fwd_bias_scaled),
+    "bias_subtracted": dict(_head_fwd=_head_fwd_bias_subtracted),
+    "bias_transposed": dict(_head_fwd=_head_fwd_bias_transposed),
+    "bias_dropped_in_bwd": dict(_head_bwd=_head_bwd_bias_dropped),
+    "bias_heads_reversed": dict(_bias_of=_bias_of_head_swapped),
 }
 
 

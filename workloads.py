@@ -40,6 +40,12 @@ WORKLOADS = {
     # long causal forward + recomputation backward, B=2 H=16 N=16384 d=128
     "long_fwd_bwd": dict(B=2, Hq=16, Hkv=16, N=16384, d=128, dtype="bf16",
                          causal=True, window=0, seed=5, bwd=True),
+    # the GQA prefill shape with a custom additive mask instead of the causal
+    # one: one fp32 [N, N] bias shared by every head, N(0, 1) values with a
+    # random 10 % of the entries -inf; forward and backward
+    "gqa_bias": dict(B=1, Hq=32, Hkv=8, N=8192, d=128, dtype="bf16", causal=False,
+                     window=0, seed=7, bwd=True, bias_shape=(1, 1, "Q", "K"),
+                     bias_masked=0.1),
 }
 
 
@@ -124,10 +130,31 @@ def make_inputs(spec, seed=None, with_grad=None):
     out["v"] = _draw(rng, ks, dtype)
     if with_grad:
         out["do"] = _draw(rng, qs, dtype)
+    if "bias_shape" in spec:
+        out["bias"] = draw_bias(rng, spec["bias_shape"], out, spec.get("bias_masked", 0.1))
     out["scale"] = spec.get("scale", 1.0 / math.sqrt(d))
     out.setdefault("causal", False)
     out.setdefault("window", 0)
     out["dtype"] = dtype
+    return out
+
+
+def draw_bias(rng, shape, geom, masked=0.1):
+    """An fp32 additive bias.  shape: four entries, each 1 (broadcast) or one
+    of "B", "H", "Q", "K" (the batch, query-head, query and key extents of
+    geom).  Values N(0, 1); a fraction `masked` of the entries is -inf, except
+    key 0 of every row, so that every row keeps a key.  Drawn in pieces of
+    16M entries (values, then the mask of the same piece)."""
+    ext = {"B": geom["B"], "H": geom["Hq"], "Q": geom["Nq"], "K": geom["Nk"]}
+    dims = tuple(ext[x] if isinstance(x, str) else int(x) for x in shape)
+    out = np.empty(dims, dtype=np.float32)
+    flat = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat.size, step):
+        n = min(step, flat.size - s)
+        flat[s:s + n] = rng.standard_normal(n, dtype=np.float32)
+        flat[s:s + n][rng.random(n, dtype=np.float32) < masked] = -np.inf
+    out[..., 0] = np.where(np.isinf(out[..., 0]), 0.0, out[..., 0])
     return out
 
 
@@ -149,6 +176,8 @@ def make_decode_inputs(spec, seed=None):
     out["q"] = _draw(rng, (B, nq, hq, d), "bf16")
     out["k"] = _draw(rng, (B, nk, hkv, d), "bf16")
     out["v"] = _draw(rng, (B, nk, hkv, d), "bf16")
+    if "bias_shape" in spec:
+        out["bias"] = draw_bias(rng, spec["bias_shape"], out, spec.get("bias_masked", 0.1))
     out["scale"] = spec.get("scale", 1.0 / math.sqrt(d))
     out["dtype"] = "bf16"
     return out
