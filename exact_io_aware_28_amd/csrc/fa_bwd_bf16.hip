@@ -450,8 +450,8 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       if constexpr (BIAS) {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          bias4_log2(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq,
-                     p.bias_vec4 != 0, &bv[4 * g]);
+          bias4(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq, p.bias_vec4 != 0,
+                kLog2e, &bv[4 * g]);
       }
       f32x16 s, dp;
 #pragma unroll

@@ -89,22 +89,20 @@ __device__ __forceinline__ uint2 pack4_t(float a0, float a1, float a2, float a3)
 }
 
 // Four consecutive entries row[j .. j+3] of an additive-bias row, times
-// log2(e) (the kernels work in log2 units).  Entries at or past `lim` and
-// rows that do not exist (row_ok false) read as 0 without touching memory;
-// `vec`: the row start is 16-byte aligned, so j % 4 == 0 allows one 128-bit
-// load.
-__device__ __forceinline__ void bias4_log2(const float* row, int j, int lim, bool row_ok,
-                                           bool vec, float* out) {
-  constexpr float kL2e = 1.4426950408889634f;
+// `mult` (log2(e): the kernels work in log2 units).  Entries at or past `lim` and rows that
+// do not exist (row_ok false) read as 0 without touching memory; `vec`: the
+// row start is 16-byte aligned, so j % 4 == 0 allows one 128-bit load.
+__device__ __forceinline__ void bias4(const float* row, int j, int lim, bool row_ok, bool vec,
+                                      float mult, float* out) {
   if (row_ok && vec && j + 4 <= lim) {
     const float4 t = *reinterpret_cast<const float4*>(row + j);
-    out[0] = t.x * kL2e;
-    out[1] = t.y * kL2e;
-    out[2] = t.z * kL2e;
-    out[3] = t.w * kL2e;
+    out[0] = t.x * mult;
+    out[1] = t.y * mult;
+    out[2] = t.z * mult;
+    out[3] = t.w * mult;
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = (row_ok && j + e < lim) ? row[j + e] * kL2e : 0.f;
+    for (int e = 0; e < 4; ++e) out[e] = (row_ok && j + e < lim) ? row[j + e] * mult : 0.f;
   }
 }
 

@@ -32,8 +32,10 @@
 //   * Causal and window masks skip whole tiles; element masks are only
 //     evaluated on tiles that straddle a boundary.
 //   * An optional additive bias (a custom mask, -inf hiding a key) is read
-//     from global memory per tile and folded into the scores in log2 units
-//     before the row maximum, so the rest of the update is unchanged.
+//     from global memory per tile, after the Q K^T products so that its
+//     registers are not live across them, and folded into the scores in
+//     log2 units before the row maximum; the rest of the update is
+//     unchanged.  The other wave of the SIMD covers the load latency.
 //   * Lazy rescaling: the running maximum used for exponentiation is only
 //     raised when a row's maximum grows by more than 2^8, so most tiles skip
 //     the accumulator rescale.  Scores stay <= 2^8 in fp32, and O and LSE
@@ -52,15 +54,8 @@ namespace {
 constexpr int kBN = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
 
-// Waves per SIMD: two, except with a bias at d = 128 (four waves per group,
-// one per SIMD), where the bias values of a tile do not fit the 256
-// registers that two waves leave each.
-template <int D, bool BIAS>
-constexpr int fwd_waves_per_simd() { return (BIAS && D == 128) ? 1 : 2; }
-
 template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BIAS>
-__global__ __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd<D, BIAS>())))
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int kWaves = W;
   constexpr int kBM = 32 * kWaves;      // query rows per work-group
@@ -178,18 +173,6 @@ void fwd_bf16_kernel(FwdParams p) {
     if (CAUSAL) need_mask = need_mask || (j0 + kBN - 1 > qlo_w + delta);
     if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
 
-    // bias of this lane's row at the keys its score elements hold; the
-    // loads are issued before the products and land while they run
-    float bv[BIAS ? NB : 1][16];
-    if constexpr (BIAS) {
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          bias4_log2(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq,
-                     p.bias_vec4 != 0, &bv[kb][4 * g]);
-    }
-
     // S^T block kb: rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4, col = qi
     f32x16 s[NB];
 #pragma unroll
@@ -216,10 +199,19 @@ void fwd_bf16_kernel(FwdParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
     if constexpr (BIAS) {
+      // bias of this lane's row at the keys its score elements hold; the
+      // fence keeps the loads (and their registers) after the products
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(s[kb][i], c, bv[kb][i]);
+        for (int g = 0; g < 4; ++g) {
+          float bv[4];
+          bias4(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq, p.bias_vec4 != 0,
+                kLog2e, bv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb][4 * g + e] = fmaf(s[kb][4 * g + e], c, bv[e]);
+        }
     }
 
     // Online-softmax update and P V product.  MASKED tiles straddle a mask
@@ -352,7 +344,7 @@ hipError_t launch_w(FwdParams p, hipStream_t stream) {
 template <int D, bool CAUSAL, bool WINDOW, bool F16>
 hipError_t launch3(const FwdParams& p, hipStream_t stream) {
   if constexpr (!F16) {  // bias: bf16, dense batches
-    if (p.bias) return launch_w<D, 4, CAUSAL, WINDOW, false, false, true>(p, stream);
+    if (p.bias) return launch_w<D, D == 128 ? 8 : 4, CAUSAL, WINDOW, false, false, true>(p, stream);
   }
   if constexpr (D == 128) {
     if (p.cu_seqlens) return launch_w<D, 8, CAUSAL, WINDOW, true, F16>(p, stream);
