@@ -31,7 +31,10 @@ Definitions used:
           is an additive bias B added to the scaled scores before the
           softmax, S = scale * Q K^T + B, with -inf entries hiding a key;
           it is a constant of the problem, so it has no gradient here, and
-          it combines with the causal and window masks.
+          it combines with the causal and window masks;
+        - dropout (fused with the rest in [llms]'s summary) acts on the
+          normalised probabilities: O = (P * Z / (1 - p)) V with Z the
+          keep-mask of oracle/philox.py; LSE is that of the undropped P.
   * the saved row statistic is the natural-log logsumexp
       LSE_i = m_i + ln(l_i) = ln(sum_j exp(S_ij))
       ([tok] "Architecture Overview" names logsumexp; [llms] "3. Recomputation
@@ -50,6 +53,8 @@ Layouts (token-major, d innermost):
 """
 
 import numpy as np
+
+from .philox import keep_mask
 
 
 def kv_head_of(h, hq, hkv):
@@ -98,16 +103,30 @@ def _softmax_rows(s):
     return p, lse
 
 
-def _head_fwd(q, k, v, scale, ok, bias=None):
+def _dropped(p, keep, p_drop):
+    """P * Z / (1 - p_drop): the probabilities that multiply V."""
+    if keep is None:
+        return p
+    return np.where(keep, p / (1.0 - p_drop), 0.0)
+
+
+def _head_fwd(q, k, v, scale, ok, bias=None, keep=None, p_drop=0.0):
     """One (sequence, head): q [nq,d], k/v [nk,d] fp64 -> O, LSE, P.
 
-    bias: None or [nq, nk], added to the scaled scores."""
+    bias: None or [nq, nk], added to the scaled scores; keep: None or the
+    boolean dropout keep-mask [nq, nk] (P is returned undropped)."""
     s = scale * (q @ k.T)
     if bias is not None:
         s = s + np.asarray(bias, np.float64)
     s = np.where(ok, s, -np.inf)
     p, lse = _softmax_rows(s)
-    return p @ v, lse, p
+    return _dropped(p, keep, p_drop) @ v, lse, p
+
+
+def _keep(dropout_p, seed, b, h, rows, nk):
+    if dropout_p == 0.0:
+        return None
+    return keep_mask(seed, b, h, rows, nk, dropout_p)
 
 
 def sequence_spans(B, N, cu_seqlens):
@@ -131,11 +150,13 @@ def _bias_of(bias, B, hq, nq, nk):
     return np.broadcast_to(bias, (B, hq, nq, nk))
 
 
-def attn_fwd(q, k, v, scale, causal=False, window=0, cu_seqlens=None, bias=None):
+def attn_fwd(q, k, v, scale, causal=False, window=0, cu_seqlens=None, bias=None,
+             dropout_p=0.0, seed=0):
     """Exact attention forward.  Returns (O, LSE) in the module's layouts.
 
     bias: None, or (dense batches only) an array that broadcasts to
-    [B, Hq, Nq, Nk], added to the scaled scores."""
+    [B, Hq, Nq, Nk], added to the scaled scores.  dropout_p, seed: dropout
+    on the probabilities with the Philox keep-mask (oracle/philox.py)."""
     dense = cu_seqlens is None
     if bias is not None and not dense:
         raise ValueError("a bias is defined for dense batches only")
@@ -162,7 +183,8 @@ def attn_fwd(q, k, v, scale, causal=False, window=0, cu_seqlens=None, bias=None)
             g = kv_head_of(h, hq, hkv)
             oh, lh, _ = _head_fwd(qp[q0:q0 + lq, h], kp[k0:k0 + lk, g],
                                   vp[k0:k0 + lk, g], scale, ok,
-                                  None if bb is None else bb[s, h])
+                                  None if bb is None else bb[s, h],
+                                  _keep(dropout_p, seed, s, h, np.arange(lq), lk), dropout_p)
             o[q0:q0 + lq, h] = oh
             if dense:
                 lse[s, h] = lh
@@ -180,12 +202,14 @@ def probabilities(q, k, scale, causal=False, window=0):
     return _softmax_rows(s)[0]
 
 
-def attn_fwd_rows(q_h, k_g, v_g, rows, scale, causal=False, window=0, bias=None):
+def attn_fwd_rows(q_h, k_g, v_g, rows, scale, causal=False, window=0, bias=None,
+                  dropout_p=0.0, seed=0, bh=(0, 0)):
     """O and LSE of selected query rows of one (sequence, head).
 
     q_h [nq,d], k_g/v_g [nk,d]; rows: indices into q_h; bias: None or this
-    head's [nq, nk] bias.  Each row is the plain definition over the whole
-    key row, so any subset of rows can be checked at any sequence length.
+    head's [nq, nk] bias; dropout_p, seed and bh = (sequence, query head)
+    select the dropout mask.  Each row is the plain definition over the
+    whole key row, so any subset of rows can be checked at any length.
     """
     q_h = np.asarray(q_h, np.float64)
     k_g = np.asarray(k_g, np.float64)
@@ -193,15 +217,18 @@ def attn_fwd_rows(q_h, k_g, v_g, rows, scale, causal=False, window=0, bias=None)
     rows = np.asarray(rows, dtype=np.int64)
     ok = _rows_allowed(rows, len(q_h), len(k_g), causal, window)
     o, lse, _ = _head_fwd(q_h[rows], k_g, v_g, scale, ok,
-                          None if bias is None else np.asarray(bias)[rows])
+                          None if bias is None else np.asarray(bias)[rows],
+                          _keep(dropout_p, seed, bh[0], bh[1], rows, len(k_g)), dropout_p)
     return o, lse
 
 
-def _head_bwd(q, k, v, do, scale, ok, bias=None):
-    """One (sequence, head) backward from the definition: returns dq, dk, dv."""
-    o, _, p = _head_fwd(q, k, v, scale, ok, bias)
-    dv = p.T @ do
-    dp = do @ v.T
+def _head_bwd(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
+    """One (sequence, head) backward from the definition: returns dq, dk, dv.
+    With dropout, O = Pd V with Pd = P * Z / (1 - p): dV = Pd^T dO and the
+    gradient reaching P is (dO V^T) * Z / (1 - p)."""
+    o, _, p = _head_fwd(q, k, v, scale, ok, bias, keep, p_drop)
+    dv = _dropped(p, keep, p_drop).T @ do
+    dp = _dropped(do @ v.T, keep, p_drop)
     dvec = (do * o).sum(axis=1)
     ds = p * (dp - dvec[:, None])
     dq = scale * (ds @ k)
@@ -209,9 +236,10 @@ def _head_bwd(q, k, v, do, scale, ok, bias=None):
     return dq, dk, dv
 
 
-def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None, bias=None):
+def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None, bias=None,
+             dropout_p=0.0, seed=0):
     """Exact gradients (dQ, dK, dV) of sum(O * dO), same layouts as Q, K, V
-    (bias as in attn_fwd, held constant)."""
+    (bias and dropout as in attn_fwd; the bias and the mask are constants)."""
     dense = cu_seqlens is None
     if bias is not None and not dense:
         raise ValueError("a bias is defined for dense batches only")
@@ -236,7 +264,8 @@ def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None, bias=N
             g = kv_head_of(h, hq, hkv)
             a, b, c = _head_bwd(qp[q0:q0 + lq, h], kp[k0:k0 + lk, g],
                                 vp[k0:k0 + lk, g], dop[q0:q0 + lq, h], scale, ok,
-                                None if bb is None else bb[s, h])
+                                None if bb is None else bb[s, h],
+                                _keep(dropout_p, seed, s, h, np.arange(lq), lk), dropout_p)
             dq[q0:q0 + lq, h] = a
             dk[k0:k0 + lk, g] += b
             dv[k0:k0 + lk, g] += c
@@ -244,7 +273,7 @@ def attn_bwd(q, k, v, do, scale, causal=False, window=0, cu_seqlens=None, bias=N
 
 
 def attn_bwd_sampled(q, k, v, do, scale, causal, window, b, g, q_rows, k_rows,
-                     chunk=2048, bias=None):
+                     chunk=2048, bias=None, dropout_p=0.0, seed=0):
     """Gradients of one dense batch entry b and KV head g, at sampled rows.
 
     Returns (dq [len(q_rows), G, d] for the G query heads of KV head g,
@@ -273,21 +302,24 @@ def attn_bwd_sampled(q, k, v, do, scale, causal, window, b, g, q_rows, k_rows,
         bh = None if bb is None else bb[b, h]
         # dQ rows: each needs only its own full row of P and dP.
         ok = _rows_allowed(q_rows, nq, nk, causal, window)
+        keep_r = _keep(dropout_p, seed, b, h, q_rows, nk)
         o_r, _, p_r = _head_fwd(qh[q_rows], kb, vb, scale, ok,
-                                None if bh is None else bh[q_rows])
-        dp_r = doh[q_rows] @ vb.T
+                                None if bh is None else bh[q_rows], keep_r, dropout_p)
+        dp_r = _dropped(doh[q_rows] @ vb.T, keep_r, dropout_p)
         dvec_r = (doh[q_rows] * o_r).sum(axis=1)
         dq[:, gi] = scale * ((p_r * (dp_r - dvec_r[:, None])) @ kb)
         # dK/dV rows: need columns k_rows of P and dS over every query row.
         for c0 in range(0, nq, chunk):
             rows = np.arange(c0, min(nq, c0 + chunk))
             okc = _rows_allowed(rows, nq, nk, causal, window)
+            keep_c = _keep(dropout_p, seed, b, h, rows, nk)
             o_c, _, p_c = _head_fwd(qh[rows], kb, vb, scale, okc,
-                                    None if bh is None else bh[rows])
+                                    None if bh is None else bh[rows], keep_c, dropout_p)
             dvec_c = (doh[rows] * o_c).sum(axis=1)
+            kj = None if keep_c is None else keep_c[:, k_rows]
             pj = p_c[:, k_rows]
-            dpj = doh[rows] @ vb[k_rows].T
+            dpj = _dropped(doh[rows] @ vb[k_rows].T, kj, dropout_p)
             dsj = pj * (dpj - dvec_c[:, None])
-            dv += pj.T @ doh[rows]
+            dv += _dropped(pj, kj, dropout_p).T @ doh[rows]
             dk += scale * (dsj.T @ qh[rows])
     return dq, dk, dv

@@ -480,6 +480,127 @@ def check_bias_backward_autograd(A):
         assert np.abs(num - g).max() <= 1e-6 * max(np.abs(num).max(), 1e-30)
 
 
+# ------------------------------------------------------------ dropout
+def check_philox_known_answers(A):
+    """The generator against its published known-answer vectors."""
+    from oracle import philox
+    n = 0
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            w = [int(x, 16) for x in line.split()]
+            got = [int(x) for x in philox.philox4x32_10(*w[:6])]
+            assert got == w[6:], (line, [hex(x) for x in got])
+            n += 1
+    assert n == 3
+
+
+def check_dropout_mask_statistics(A):
+    """The keep fraction is 1 - p within binomial error, masks of different
+    heads, sequences and seeds differ, and every output word is used."""
+    from oracle import philox
+    for p in (0.1, 0.5, 0.9):
+        m = philox.keep_mask(123, 1, 2, np.arange(256), 256, p)
+        n = m.size
+        assert abs(m.mean() - (1 - p)) < 5 * math.sqrt(p * (1 - p) / n)
+    a = philox.keep_mask(7, 0, 0, np.arange(64), 64, 0.5)
+    for other in (philox.keep_mask(7, 0, 1, np.arange(64), 64, 0.5),
+                  philox.keep_mask(7, 1, 0, np.arange(64), 64, 0.5),
+                  philox.keep_mask(8, 0, 0, np.arange(64), 64, 0.5),
+                  philox.keep_mask(7 + (1 << 32), 0, 0, np.arange(64), 64, 0.5)):
+        assert 0.3 < (a != other).mean() < 0.7
+    # keys 4t .. 4t+3 come from different words: not all equal within groups
+    g = a.reshape(64, 16, 4)
+    assert (g != g[..., :1]).any(axis=2).mean() > 0.5
+    # rows restricted to a subset agree with the full mask
+    assert np.array_equal(philox.keep_mask(7, 0, 0, [5, 40], 64, 0.5), a[[5, 40]])
+    assert philox.keep_mask(7, 0, 0, np.arange(8), 64, 0.0).all()
+
+
+def _torch_dropout_reference(q, k, v, scale, causal, keep, p):
+    """O = (softmax(S) * Z / (1 - p)) V in float64 torch, one head [n, d]."""
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    s = scale * tq @ tk.T
+    if causal:
+        n, m = s.shape
+        s = s.masked_fill(torch.ones(n, m, dtype=torch.bool).triu(m - n + 1), float("-inf"))
+    pr = torch.softmax(s, dim=1)
+    return (pr * torch.from_numpy(keep.astype(np.float64)) / (1 - p)) @ tv
+
+
+def check_dropout_matches_masked_softmax(A):
+    """Forward with dropout equals torch's softmax times the keep-mask over
+    1 - p, times V; LSE is that of the undropped scores; p = 0 (or a p whose
+    threshold is 0) is plain attention."""
+    from oracle import philox
+    rng = _rng(45)
+    q, k, v = _dense(rng, 2, 13, 18, 4, 2, 8)
+    for causal, p in [(False, 0.3), (True, 0.6)]:
+        o, lse = A.attn_fwd(q, k, v, 0.5, causal, dropout_p=p, seed=99)
+        _, lse0 = A.attn_fwd(q, k, v, 0.5, causal)
+        assert np.allclose(lse, lse0, atol=1e-12)
+        for b in range(2):
+            for h in range(4):
+                keep = philox.keep_mask(99, b, h, np.arange(13), 18, p)
+                ref = _torch_dropout_reference(q[b, :, h], k[b, :, h // 2], v[b, :, h // 2],
+                                               0.5, causal, keep, p).numpy()
+                assert np.allclose(o[b, :, h], ref, atol=1e-12)
+    o1, _ = A.attn_fwd(q, k, v, 0.5, True, dropout_p=1e-12, seed=5)
+    o2, _ = A.attn_fwd(q, k, v, 0.5, True)
+    assert np.allclose(o1, o2, atol=1e-10)
+
+
+def check_dropout_unbiased(A):
+    """Averaged over many seeds the dropped output approaches the plain one
+    (E[Z] / (1 - p) = 1), within five standard errors."""
+    rng = _rng(46)
+    q, k, v = _dense(rng, 1, 6, 9, 1, 1, 4)
+    o0, _ = A.attn_fwd(q, k, v, 0.7)
+    outs = np.stack([A.attn_fwd(q, k, v, 0.7, dropout_p=0.4, seed=s)[0] for s in range(600)])
+    err = np.abs(outs.mean(axis=0) - o0)
+    se = outs.std(axis=0) / math.sqrt(len(outs))
+    assert np.all(err <= 5 * se + 1e-12)
+
+
+def check_dropout_backward(A):
+    """Gradients with dropout against torch autograd through the masked
+    softmax (same keep-mask), and central finite differences."""
+    from oracle import philox
+    rng = _rng(47)
+    q, k, v = _dense(rng, 1, 10, 14, 2, 1, 6)
+    do = rng.standard_normal(q.shape)
+    p = 0.35
+    dq, dk, dv = A.attn_bwd(q, k, v, do, 0.6, True, dropout_p=p, seed=11)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    loss = 0
+    for h in range(2):
+        keep = philox.keep_mask(11, 0, h, np.arange(10), 14, p)
+        s = 0.6 * tq[0, :, h] @ tk[0, :, 0].T
+        s = s.masked_fill(torch.ones(10, 14, dtype=torch.bool).triu(5), float("-inf"))
+        o = (torch.softmax(s, 1) * torch.from_numpy(keep.astype(np.float64)) / (1 - p)) @ tv[0, :, 0]
+        loss = loss + (o * torch.from_numpy(do[0, :, h])).sum()
+    loss.backward()
+    assert np.allclose(dq, tq.grad.numpy(), atol=1e-11)
+    assert np.allclose(dk, tk.grad.numpy(), atol=1e-11)
+    assert np.allclose(dv, tv.grad.numpy(), atol=1e-11)
+    q, k, v = _dense(rng, 1, 5, 6, 1, 1, 3)
+    do = rng.standard_normal(q.shape)
+    dq, dk, dv = A.attn_bwd(q, k, v, do, 0.8, False, dropout_p=0.5, seed=3)
+    f = lambda: float((A.attn_fwd(q, k, v, 0.8, dropout_p=0.5, seed=3)[0] * do).sum())
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x[idx] += h
+            fp = f()
+            x[idx] -= 2 * h
+            fm = f()
+            x[idx] += h
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.abs(num - g).max() <= 1e-6 * max(np.abs(num).max(), 1e-30)
+
+
 ALL_FORWARD = [check_rows_sum_to_one, check_identical_keys, check_dominant_score,
                check_permutation_invariance, check_lse_is_logsumexp,
                check_scale_zero, check_against_torch_sdpa, check_brute_force_tiny,
@@ -488,6 +609,9 @@ ALL_FORWARD = [check_rows_sum_to_one, check_identical_keys, check_dominant_score
                check_causal_row_zero, check_chunked_prefill_alignment,
                check_empty_rows, check_bias_against_torch_sdpa,
                check_bias_row_constant, check_bias_is_key_shift,
-               check_bias_mask_equals_causal]
+               check_bias_mask_equals_causal, check_philox_known_answers,
+               check_dropout_mask_statistics, check_dropout_matches_masked_softmax,
+               check_dropout_unbiased]
 ALL_BACKWARD = [check_backward_finite_differences, check_backward_autograd,
-                check_backward_invariants, check_bias_backward_autograd]
+                check_backward_invariants, check_bias_backward_autograd,
+                check_dropout_backward]

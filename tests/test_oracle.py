@@ -80,58 +80,82 @@ def _lse_without_max(s):
     return p, lse - np.where(np.isfinite(m), m, 0.0)
 
 
-def _head_fwd_no_scale(q, k, v, scale, ok, bias=None):
+def _head_fwd_no_scale(q, k, v, scale, ok, bias=None, keep=None, p_drop=0.0):
     s = q @ k.T + (0.0 if bias is None else bias)
     s = np.where(ok, s, -np.inf)
     p, lse = A._softmax_rows(s)
-    return p @ v, lse, p
+    return A._dropped(p, keep, p_drop) @ v, lse, p
 
 
-def _head_bwd_missing_D(q, k, v, do, scale, ok, bias=None):
-    o, _, p = A._head_fwd(q, k, v, scale, ok, bias)
+def _head_bwd_missing_D(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
+    o, _, p = A._head_fwd(q, k, v, scale, ok, bias, keep, p_drop)
     ds = p * (do @ v.T)
     return scale * (ds @ k), scale * (ds.T @ q), p.T @ do
 
 
-def _head_bwd_unscaled_dk(q, k, v, do, scale, ok, bias=None):
-    dq, dk, dv = A._head_bwd(q, k, v, do, scale, ok, bias)
+def _head_bwd_unscaled_dk(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
+    dq, dk, dv = A._head_bwd(q, k, v, do, scale, ok, bias, keep, p_drop)
     return dq, dk / scale, dv
 
 
-def _head_bwd_transposed_dv(q, k, v, do, scale, ok, bias=None):
-    dq, dk, _ = A._head_bwd(q, k, v, do, scale, ok, bias)
-    _, _, p = A._head_fwd(q, k, v, scale, ok, bias)
+def _head_bwd_transposed_dv(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
+    dq, dk, _ = A._head_bwd(q, k, v, do, scale, ok, bias, keep, p_drop)
+    _, _, p = A._head_fwd(q, k, v, scale, ok, bias, keep, p_drop)
     return dq, dk, p @ do  # P instead of P^T (the pins use square shapes)
 
 
-def _head_fwd_bias_scaled(q, k, v, scale, ok, bias=None):
+def _head_fwd_bias_scaled(q, k, v, scale, ok, bias=None, keep=None, p_drop=0.0):
     s = scale * (q @ k.T + (0.0 if bias is None else bias))
     p, lse = A._softmax_rows(np.where(ok, s, -np.inf))
-    return p @ v, lse, p
+    return A._dropped(p, keep, p_drop) @ v, lse, p
 
 
-def _head_fwd_bias_subtracted(q, k, v, scale, ok, bias=None):
+def _head_fwd_bias_subtracted(q, k, v, scale, ok, bias=None, keep=None, p_drop=0.0):
     s = scale * (q @ k.T) - (0.0 if bias is None else bias)
     p, lse = A._softmax_rows(np.where(ok, s, -np.inf))
-    return p @ v, lse, p
+    return A._dropped(p, keep, p_drop) @ v, lse, p
 
 
-def _head_fwd_bias_transposed(q, k, v, scale, ok, bias=None):
+def _head_fwd_bias_transposed(q, k, v, scale, ok, bias=None, keep=None, p_drop=0.0):
     b = 0.0 if bias is None else np.asarray(bias)
     if np.ndim(b) == 2 and b.shape[0] == b.shape[1]:
         b = b.T
     p, lse = A._softmax_rows(np.where(ok, scale * (q @ k.T) + b, -np.inf))
-    return p @ v, lse, p
+    return A._dropped(p, keep, p_drop) @ v, lse, p
 
 
-def _head_bwd_bias_dropped(q, k, v, do, scale, ok, bias=None):
-    return A._head_bwd(q, k, v, do, scale, ok, None)
+def _head_bwd_bias_dropped(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
+    return A._head_bwd(q, k, v, do, scale, ok, None, keep, p_drop)
 
 
 def _bias_of_head_swapped(bias, B, hq, nq, nk):
     if bias is None:
         return None
     return np.broadcast_to(bias, (B, hq, nq, nk))[:, ::-1]
+
+
+def _dropped_unscaled(p, keep, p_drop):
+    return p if keep is None else np.where(keep, p, 0.0)
+
+
+def _keep_rows_keys_swapped(dropout_p, seed, b, h, rows, nk):
+    if dropout_p == 0.0:
+        return None
+    from oracle import philox
+    rows = np.asarray(rows)
+    j = np.arange(nk)
+    w = philox.philox4x32_10(rows[:, None] >> 2, j[None, :], h, b, seed & 0xFFFFFFFF, seed >> 32)
+    e = (rows & 3)[:, None]
+    u = np.select([e == 0, e == 1, e == 2, e == 3], w)
+    return u >= np.uint64(philox.drop_threshold(dropout_p))
+
+
+def _head_bwd_dropout_dp_unmasked(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
+    o, _, p = A._head_fwd(q, k, v, scale, ok, bias, keep, p_drop)
+    dv = A._dropped(p, keep, p_drop).T @ do
+    dp = do @ v.T
+    ds = p * (dp - (do * o).sum(axis=1)[:, None])
+    return scale * (ds @ k), scale * (ds.T @ q), dv
 
 
 MUTATIONS = {
@@ -149,6 +173,9 @@ MUTATIONS = {
     "bias_transposed": dict(_head_fwd=_head_fwd_bias_transposed),
     "bias_dropped_in_bwd": dict(_head_bwd=_head_bwd_bias_dropped),
     "bias_heads_reversed": dict(_bias_of=_bias_of_head_swapped),
+    "dropout_unscaled": dict(_dropped=_dropped_unscaled),
+    "dropout_rows_keys_swapped": dict(_keep=_keep_rows_keys_swapped),
+    "dropout_dp_unmasked": dict(_head_bwd=_head_bwd_dropout_dp_unmasked),
 }
 
 
@@ -275,3 +302,32 @@ def test_f16_inputs_are_exact_halves():
         assert np.array_equal(x.astype(np.float16).astype(np.float32), x)
         # not merely bf16 values: fp16 keeps bits that bf16 drops
         assert not np.array_equal(workloads.round_bf16(x), x)
+
+
+def test_sampled_paths_with_bias_and_dropout():
+    """The row-sampled forward and backward agree with the full ones when a
+    bias and dropout are on."""
+    rng = np.random.default_rng(35)
+    q = rng.standard_normal((2, 40, 4, 8))
+    k = rng.standard_normal((2, 40, 2, 8))
+    v = rng.standard_normal((2, 40, 2, 8))
+    do = rng.standard_normal(q.shape)
+    bias = rng.standard_normal((2, 1, 40, 40))
+    kw = dict(bias=bias, dropout_p=0.3, seed=77)
+    o, lse = A.attn_fwd(q, k, v, 0.3, True, 0, **kw)
+    rows = np.array([0, 9, 39])
+    for b in range(2):
+        for h in range(4):
+            orow, lrow = A.attn_fwd_rows(q[b, :, h], k[b, :, h // 2], v[b, :, h // 2], rows, 0.3,
+                                         True, 0, bias=bias[b, 0], dropout_p=0.3, seed=77,
+                                         bh=(b, h))
+            assert np.allclose(orow, o[b, rows, h], atol=1e-12)
+            assert np.allclose(lrow, lse[b, h, rows], atol=1e-12)
+    dq, dk, dv = A.attn_bwd(q, k, v, do, 0.3, True, 0, **kw)
+    qr, kr = np.array([0, 5, 39]), np.array([0, 17, 39])
+    for b in range(2):
+        for g in range(2):
+            sq, sk, sv = A.attn_bwd_sampled(q, k, v, do, 0.3, True, 0, b, g, qr, kr, chunk=13, **kw)
+            assert np.allclose(sq, dq[b][qr][:, 2 * g:2 * g + 2], atol=1e-12)
+            assert np.allclose(sk, dk[b, kr, g], atol=1e-12)
+            assert np.allclose(sv, dv[b, kr, g], atol=1e-12)
