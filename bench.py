@@ -148,6 +148,9 @@ def time_forward(inp, dev, steps, warmup):
         bias = dev["bias"]
         kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"])
         fn = lambda q, k, v, **a: fa.fa_fwd_bias(q, k, v, bias, **a)
+    if inp.get("dropout_p"):
+        dp, ds = inp["dropout_p"], inp["dropout_seed"]
+        fn = lambda q, k, v, **a: fa.fa_fwd_dropout(q, k, v, dp, ds, **a)
     o, lse = fn(dev["q"], dev["k"], dev["v"], **kw)
     for _ in range(warmup):
         fn(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)
@@ -173,6 +176,11 @@ def time_backward(inp, dev, steps, warmup):
         kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"])
         fwd = lambda q, k, v, **a: fa.fa_fwd_bias(q, k, v, bias, **a)
         bwd = lambda q, k, v, o, do, lse, **a: fa.fa_bwd_bias(q, k, v, bias, o, do, lse, **a)
+    if inp.get("dropout_p"):
+        dp, ds = inp["dropout_p"], inp["dropout_seed"]
+        fwd = lambda q, k, v, **a: fa.fa_fwd_dropout(q, k, v, dp, ds, **a)
+        bwd = lambda q, k, v, o, do, lse, **a: fa.fa_bwd_dropout(q, k, v, o, do, lse, dp, ds,
+                                                                 **a)
     o, lse = fwd(dev["q"], dev["k"], dev["v"], **kw)
     do = torch.from_numpy(inp["do"]).to(torch.bfloat16).cuda()
     dq, dk, dv = bwd(dev["q"], dev["k"], dev["v"], o, do, lse, **kw)

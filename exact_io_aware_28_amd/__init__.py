@@ -66,6 +66,14 @@ def lib():
         L.fa_bwd_bias.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                   i, i, i, i, i, i, f, i, i, vp, i64, i64, i64, vp]
         L.fa_bwd_bias.restype = i
+        u64 = ctypes.c_uint64
+        L.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, f,
+                                     u64, vp]
+        L.fa_fwd_dropout.restype = i
+        L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, i, i, i, i, i, i, f, i, i, vp, f, u64,
+                                     vp]
+        L.fa_bwd_dropout.restype = i
         L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
         L.fa_decode_workspace_size.restype = ctypes.c_size_t
         L.fa_decode_num_splits.argtypes = [i, i, i, i, i]
@@ -196,6 +204,58 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
                       int(window), _ptr(cu_seqlens), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_fwd_dropout(q, k, v, dropout_p, seed, scale=None, causal=False, window=0,
+                   cu_seqlens=None, max_seqlen=None, out=None, lse=None, stream=None):
+    """bf16 forward with dropout on the probabilities (Philox keep-mask of
+    the public header); returns (o bf16, lse fp32 of the undropped P).
+    dropout_p is passed as a C float."""
+    import torch
+    _check({"q": q, "k": k, "v": v}, torch.bfloat16)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty(_lse_shape(q, B, hq, nq, cu_seqlens), dtype=torch.float32,
+                          device=q.device)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    st = lib().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv,
+                              nq, nk, d, float(scale), int(bool(causal)), int(window),
+                              _ptr(cu_seqlens), float(dropout_p), int(seed), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_dropout")
+    return out, lse
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dropout_p, seed, scale=None, causal=False,
+                   window=0, cu_seqlens=None, max_seqlen=None, dq=None, dk=None, dv=None,
+                   workspace=None, stream=None):
+    """bf16 backward of fa_fwd_dropout (same dropout_p and seed); returns
+    (dq, dk, dv)."""
+    import torch
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, torch.bfloat16)
+    _check({"lse": lse}, torch.float32)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lib().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(),
+                              B, hq, hkv, nq, nk, d, float(scale), int(bool(causal)),
+                              int(window), _ptr(cu_seqlens), float(dropout_p), int(seed),
+                              _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dropout")
     return dq, dk, dv
 
 

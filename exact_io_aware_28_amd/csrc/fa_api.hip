@@ -66,7 +66,20 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
   p.bias = nullptr;
   p.bias_sb = p.bias_sh = p.bias_sq = 0;
   p.bias_vec4 = 0;
+  p.dropout = 0;
+  p.drop_thresh = 0;
+  p.seed_lo = p.seed_hi = 0;
+  p.drop_scale = 1.0f;
   return p;
+}
+
+// Dropout probability in [0, 1): integer threshold floor(p * 2^32) (a key
+// is dropped iff its 32-bit Philox word is below it) and the scale 1/(1-p).
+int check_dropout(float dropout_p, uint32_t* thresh, float* scale) {
+  if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;  // also NaN
+  *thresh = (uint32_t)((double)dropout_p * 4294967296.0);
+  *scale = (float)(1.0 / (1.0 - (double)dropout_p));
+  return FA_OK;
 }
 
 // An additive bias: non-null, 4-byte aligned, non-negative element strides.
@@ -156,7 +169,8 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o,
                     void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
                     int Nk, int d, float scale, int causal, int window,
                     const int32_t* cu_seqlens, const float* bias, int64_t sb, int64_t sh,
-                    int64_t sq, int has_bias, void* stream) {
+                    int64_t sq, int has_bias, void* stream, float dropout_p = 0.0f,
+                    uint64_t seed = 0) {
   const void* t[] = {q, k, v, o, dout, dq, dk, dv, workspace};
   const float* s[] = {lse};
   int st = check_common(t, 9, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
@@ -167,9 +181,18 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o,
     st = check_bias(bias, sb, sh, sq, &vec4);
     if (st != FA_OK) return st;
   }
+  uint32_t thresh = 0;
+  float drop_scale = 1.0f;
+  st = check_dropout(dropout_p, &thresh, &drop_scale);
+  if (st != FA_OK) return st;
   // packed batches: T <= B * Nq (each sequence is at most Nq long)
   if (workspace_bytes < fa_bwd_workspace_size(B * Nq, Hq, d)) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
+  p.dropout = dropout_p > 0.0f;
+  p.drop_thresh = thresh;
+  p.drop_scale = drop_scale;
+  p.seed_lo = (uint32_t)seed;
+  p.seed_hi = (uint32_t)(seed >> 32);
   p.bias = has_bias ? bias : nullptr;
   p.bias_sb = sb;
   p.bias_sh = sh;
@@ -217,6 +240,39 @@ int fa_bwd_bias(const void* q, const void* k, const void* v, const void* o, cons
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
                   Nq, Nk, d, scale, causal, window, nullptr, bias, bias_stride_b,
                   bias_stride_h, bias_stride_q, 1, stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int window, const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                   void* stream) {
+  const void* t[] = {q, k, v, o};
+  const float* s[] = {lse};
+  int st = check_common(t, 4, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                        cu_seqlens, 64);
+  if (st != FA_OK) return st;
+  uint32_t thresh = 0;
+  float drop_scale = 1.0f;
+  st = check_dropout(dropout_p, &thresh, &drop_scale);
+  if (st != FA_OK) return st;
+  fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                               window, cu_seqlens);
+  p.dropout = dropout_p > 0.0f;  // p = 0 keeps every key: the plain kernel
+  p.drop_thresh = thresh;
+  p.drop_scale = drop_scale;
+  p.seed_lo = (uint32_t)seed;
+  p.seed_hi = (uint32_t)(seed >> 32);
+  return fa::launch_fwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                   int Nk, int d, float scale, int causal, int window,
+                   const int32_t* cu_seqlens, float dropout_p, uint64_t seed, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                  Nq, Nk, d, scale, causal, window, cu_seqlens, nullptr, 0, 0, 0, 0, stream,
+                  dropout_p, seed);
 }
 
 // Split-KV workspace: normalised partial outputs [num_splits][B][Nq][Hq][d]

@@ -27,6 +27,11 @@
 //      reduction.
 // All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the
 // probability and dS tiles are rounded to bf16 as MFMA operands.
+// With dropout (keep-mask Z regenerated from the seed, never stored):
+//     dV = (P Z / (1 - p))^T dO,  dS = P (dP Z / (1 - p) - D),
+// and D = rowsum(dO * O) is unchanged, O being the dropped output.  The dQ
+// kernel (one query row per lane, runs of four keys) draws one Philox call
+// per four elements; the dK/dV kernel (one key per lane) one per element.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 template <int D>
 constexpr int dkdv_waves_per_simd() { return D == 64 ? 2 : 1; }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(dkdv_waves_per_simd<D>())))
 void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
@@ -195,6 +200,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
   auto compute = [&](int it, const __bf16* tq, const __bf16* tdo, const float* tl,
                      const float* td) {
     const int i0 = q_lo + (it % n_qt) * kQTile;
+    const int h_it = hkv * G + it / n_qt;  // query head of this tile
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qr0 = i0 + qb * 32;
@@ -248,8 +254,17 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
             float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - Lv[e] : -Lv[e]));
             if (MASKED)
               pv = visible<CAUSAL, WINDOW>(i0 + qrow + e, kj, delta, sp.lk, p.window) ? pv : 0.f;
-            s[i] = pv;
-            dp[i] = pv * (dp[i] - Dv[e]);
+            if constexpr (DROP) {
+              // O = (P Z / (1 - p)) V: dV takes the dropped, rescaled P and
+              // the gradient reaching P is dP Z / (1 - p)
+              const bool kp = keep1(kj, i0 + qrow + e, h_it, b, p.seed_lo, p.seed_hi,
+                                    p.drop_thresh);
+              s[i] = kp ? pv * p.drop_scale : 0.f;
+              dp[i] = pv * ((kp ? dp[i] * p.drop_scale : 0.f) - Dv[e]);
+            } else {
+              s[i] = pv;
+              dp[i] = pv * (dp[i] - Dv[e]);
+            }
           }
         }
       };
@@ -328,7 +343,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 template <int D, bool CAUSAL, bool WINDOW, bool BIAS>
 constexpr int dq_waves_per_simd() { return (D == 128 && ((!CAUSAL && !WINDOW) || BIAS)) ? 1 : 2; }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<D, CAUSAL, WINDOW, BIAS>())))
 void bwd_dq_kernel(BwdParams p, int num_qtiles) {
@@ -475,6 +490,14 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       // base + off with off = 8(i/4) + i%4
       const int base = j0 + kb * 32 + 4 * hl;
       const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
+      // dropout: keep bits of the four runs of four keys base + 8r + {0..3}
+      uint32_t keep = 0xFFFF;
+      if constexpr (DROP) {
+        keep = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          keep |= keep4(base + 8 * r, qi, h, b, p.seed_lo, p.seed_hi, p.drop_thresh) << (4 * r);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - lse2 : -lse2));
@@ -485,7 +508,10 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
           if (WINDOW) ok = ok && off > lo;
           pv = ok ? pv : 0.f;
         }
-        dp[i] = pv * (dp[i] - dq_d);
+        if constexpr (DROP)
+          dp[i] = pv * ((((keep >> i) & 1) ? dp[i] * p.drop_scale : 0.f) - dq_d);
+        else
+          dp[i] = pv * (dp[i] - dq_d);
       }
 
       // dQ^T += K^T dS^T over this half's two 16-key chunks (same key
@@ -538,15 +564,15 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   }
 }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false, bool DROP = false>
 hipError_t launch4(const BwdParams& p, hipStream_t stream) {
   const int nkt = (p.Nk + kKeyBlock - 1) / kKeyBlock;
   const int nqt = (p.Nq + kQBlock - 1) / kQBlock;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
                      dim3((unsigned)p.B * p.Hkv * nkt), dim3(kThreads), 0, stream, p, nkt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS>),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
                      dim3((unsigned)p.B * p.Hq * nqt), dim3(kThreads), 0, stream, p, nqt);
   return hipGetLastError();
 }
@@ -554,6 +580,9 @@ hipError_t launch4(const BwdParams& p, hipStream_t stream) {
 template <int D, bool CAUSAL, bool WINDOW>
 hipError_t launch3(const BwdParams& p, hipStream_t stream) {
   if (p.bias) return launch4<D, CAUSAL, WINDOW, false, true>(p, stream);  // dense only
+  if (p.dropout)  // no bias
+    return p.cu_seqlens ? launch4<D, CAUSAL, WINDOW, true, false, true>(p, stream)
+                        : launch4<D, CAUSAL, WINDOW, false, false, true>(p, stream);
   return p.cu_seqlens ? launch4<D, CAUSAL, WINDOW, true>(p, stream)
                       : launch4<D, CAUSAL, WINDOW, false>(p, stream);
 }

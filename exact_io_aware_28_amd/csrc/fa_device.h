@@ -288,6 +288,52 @@ __device__ __forceinline__ int64_t lse_index(const int32_t* cu, int B, int Hq,
   return ((int64_t)b * Hq + h) * Nq + i;
 }
 
+// ---------------------------------------------------------------- dropout
+// Counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).  Per round the
+// counter words (c0, c1, c2, c3) become
+//     (hi(B * c2) ^ c1 ^ k0,  lo(B * c2),  hi(A * c0) ^ c3 ^ k1,  lo(A * c0))
+// with A = 0xD2511F53, B = 0xCD9E8D57 and 64-bit products; the key (k0, k1)
+// advances by (0x9E3779B9, 0xBB67AE85) between rounds.  The key is uniform
+// over the wave (scalar registers); the counter is per lane.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t a = (uint64_t)0xD2511F53u * c0;
+    const uint64_t m = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(m >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(a >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)m;
+    c3 = (uint32_t)a;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// Keep bits of the dropout mask for keys j4 .. j4 + 3 (j4 % 4 == 0) of query
+// row i of (sequence b, query head h): bit e is set iff key j4 + e is kept.
+__device__ __forceinline__ uint32_t keep4(int j4, int i, int h, int b, uint32_t seed_lo,
+                                          uint32_t seed_hi, uint32_t thresh) {
+  const uint4 w = philox4x32_10((uint32_t)j4 >> 2, (uint32_t)i, (uint32_t)h, (uint32_t)b,
+                                seed_lo, seed_hi);
+  return (uint32_t)(w.x >= thresh) | ((uint32_t)(w.y >= thresh) << 1) |
+         ((uint32_t)(w.z >= thresh) << 2) | ((uint32_t)(w.w >= thresh) << 3);
+}
+
+// Keep bit of the single element (i, j) of (b, h).
+__device__ __forceinline__ bool keep1(int j, int i, int h, int b, uint32_t seed_lo,
+                                      uint32_t seed_hi, uint32_t thresh) {
+  const uint4 w = philox4x32_10((uint32_t)j >> 2, (uint32_t)i, (uint32_t)h, (uint32_t)b,
+                                seed_lo, seed_hi);
+  const int e = j & 3;
+  const uint32_t x = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+  return x >= thresh;
+}
+
 // Visibility of key j from query i (sequence-relative), delta = lk - lq.
 template <bool CAUSAL, bool WINDOW>
 __device__ __forceinline__ bool visible(int i, int j, int delta, int lk,

@@ -36,6 +36,12 @@
 //     registers are not live across them, and folded into the scores in
 //     log2 units before the row maximum; the rest of the update is
 //     unchanged.  The other wave of the SIMD covers the load latency.
+//   * Optional dropout on the probabilities (inferensys.com glossary
+//     "FlashAttention", the paragraph on the one fused kernel: matrix
+//     multiply, softmax, dropout and masking): a Philox4x32-10 call per run
+//     of four keys gives the keep bits; dropped probabilities still count
+//     in l (the softmax is of the undropped scores), the kept ones go to the
+//     P V product and 1 / (1 - p) is folded into the final division by l.
 //   * Lazy rescaling: the running maximum used for exponentiation is only
 //     raised when a row's maximum grows by more than 2^8, so most tiles skip
 //     the accumulator rescale.  Scores stay <= 2^8 in fp32, and O and LSE
@@ -54,7 +60,8 @@ namespace {
 constexpr int kBN = 64;   // keys per K/V tile
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unrescaled score
 
-template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BIAS>
+template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BIAS,
+          bool DROP>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int kWaves = W;
@@ -268,6 +275,13 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < NC; ++kc) {
         const int kb = kc >> 1, i0 = (kc & 1) * 8;
+        // dropout: keep bits of the chunk's two runs of four keys (the
+        // normaliser l sums the undropped probabilities)
+        uint32_t keep = 0xFF;
+        if constexpr (DROP)
+          keep = keep4(key_of(kb, i0), qi, h, b, p.seed_lo, p.seed_hi, p.drop_thresh) |
+                 (keep4(key_of(kb, i0 + 4), qi, h, b, p.seed_lo, p.seed_hi, p.drop_thresh)
+                  << 4);
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -279,6 +293,7 @@ void fwd_bf16_kernel(FwdParams p) {
             lsum1 += pv[e];
           else
             lsum0 += pv[e];
+          if constexpr (DROP) pv[e] = ((keep >> e) & 1) ? pv[e] : 0.f;
         }
         const bf16x8 pb = pack8_t<F16>(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         bf16x8 va[DB];
@@ -312,7 +327,8 @@ void fwd_bf16_kernel(FwdParams p) {
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
   const float l_tot = l_run + xor32(l_run);
   if (qi < sp.lq) {
-    const float inv = (l_tot == 0.f) ? 0.f : 1.0f / l_tot;
+    // dropout scales the kept probabilities by 1 / (1 - p)
+    const float inv = (l_tot == 0.f) ? 0.f : (DROP ? p.drop_scale : 1.0f) / l_tot;
     __bf16* op = (__bf16*)p.o + (sp.q0 + qi) * qstride + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -332,19 +348,25 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 // Launch with W waves per work-group; the query-tile count follows from W.
-template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BIAS = false>
+template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BIAS = false,
+          bool DROP = false>
 hipError_t launch_w(FwdParams p, hipStream_t stream) {
   p.num_qtiles = (p.Nq + 32 * W - 1) / (32 * W);
   dim3 grid((unsigned)p.B * p.Hq * p.num_qtiles), block(64 * W);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, WINDOW, VARLEN, F16, BIAS>), grid, block,
-                     0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, WINDOW, VARLEN, F16, BIAS, DROP>), grid,
+                     block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool WINDOW, bool F16>
 hipError_t launch3(const FwdParams& p, hipStream_t stream) {
-  if constexpr (!F16) {  // bias: bf16, dense batches
-    if (p.bias) return launch_w<D, D == 128 ? 8 : 4, CAUSAL, WINDOW, false, false, true>(p, stream);
+  if constexpr (!F16) {  // bias: bf16, dense batches; dropout: bf16, no bias
+    constexpr int W = D == 128 ? 8 : 4;
+    if (p.bias) return launch_w<D, W, CAUSAL, WINDOW, false, false, true>(p, stream);
+    if (p.dropout) {
+      if (p.cu_seqlens) return launch_w<D, W, CAUSAL, WINDOW, true, false, false, true>(p, stream);
+      return launch_w<D, W, CAUSAL, WINDOW, false, false, false, true>(p, stream);
+    }
   }
   if constexpr (D == 128) {
     if (p.cu_seqlens) return launch_w<D, 8, CAUSAL, WINDOW, true, F16>(p, stream);

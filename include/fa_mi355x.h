@@ -184,6 +184,39 @@ int fa_bwd_bias(const void* q, const void* k, const void* v, const void* o,
                 int64_t bias_stride_q, void* stream);
 
 /*
+ * Forward and backward with dropout on the attention probabilities
+ * (inferensys.com glossary "FlashAttention", the paragraph on the single
+ * fused kernel, lists dropout among the operations fused into one pass).  O = (P * Z / (1 - dropout_p)) V, where P is the
+ * softmax of fa_fwd and Z is a 0/1 keep-mask; LSE is that of the undropped P
+ * (as fa_fwd), so fa_bwd_dropout rebuilds P from it and regenerates Z
+ * instead of storing it.  Gradients: dV = (P Z / (1 - p))^T dO,
+ * dP = (dO V^T) Z / (1 - p), D_i = sum_c dO_ic O_ic, dS = P (dP - D).
+ * The pages fix no random number generator; this library's mask is:
+ *   element (b, h, i, j) -- batch entry or packed sequence b, query head h,
+ *   query row i and key j counted from the start of the sequence -- is kept
+ *   iff word (j mod 4) of Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+ *   "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) at counter
+ *   (floor(j / 4), i, h, b) with key (seed mod 2^32, floor(seed / 2^32)) is
+ *   >= floor(dropout_p * 2^32), dropout_p taken as a double.
+ * The same seed and dropout_p must be passed to the forward and the
+ * backward.  dropout_p = 0 gives exactly fa_fwd / fa_bwd.  Other arguments,
+ * layouts and errors as fa_fwd and fa_bwd (dense or packed batches), plus
+ * FA_ERR_INVALID_ARG for dropout_p outside [0, 1) or NaN.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   float scale, int causal, int window,
+                   const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                   void* stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   float scale, int causal, int window,
+                   const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                   void* stream);
+
+/*
  * Split-KV attention for a few query rows per sequence over a long key/value
  * cache: single-token decode and short chunked prefill, where the cost is
  * streaming the cached keys and values (klaylearn.com glossary

@@ -8,6 +8,7 @@ Sources (the pages this follows):
           Solved Transformer Memory Bottlenecks"
   [tok]   tokrepo.com, "Flash Attention - Fast Memory-Efficient Exact Attention"
   [klay]  klaylearn.com glossary, "flash-attention"
+  [inf]   inferensys.com glossary, "FlashAttention"
 
 Definitions used:
   * S = scale * Q K^T, P = softmax(S) row-wise, O = P V
@@ -32,8 +33,8 @@ Definitions used:
           softmax, S = scale * Q K^T + B, with -inf entries hiding a key;
           it is a constant of the problem, so it has no gradient here, and
           it combines with the causal and window masks;
-        - dropout (fused with the rest in [llms]'s summary) acts on the
-          normalised probabilities: O = (P * Z / (1 - p)) V with Z the
+        - dropout (fused with the rest in [inf]'s fused-kernel paragraph)
+          acts on the normalised probabilities: O = (P * Z / (1 - p)) V with Z the
           keep-mask of oracle/philox.py; LSE is that of the undropped P.
   * the saved row statistic is the natural-log logsumexp
       LSE_i = m_i + ln(l_i) = ln(sum_j exp(S_ij))

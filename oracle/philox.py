@@ -2,10 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-The pages put dropout inside the fused attention operation (llms.blog,
-"FlashAttention: How IO-Aware Tiling and Online Softmax Solved Transformer
-Memory Bottlenecks", the opening summary of what is fused) but fix no random
-number generator.  Reading taken here: the mask is drawn from the
+The pages put dropout inside the fused attention operation (inferensys.com
+glossary "FlashAttention", the paragraph on the single fused kernel: matrix
+multiply, softmax, dropout and masking in one pass) but fix no random number
+generator.  Reading taken here: the mask is drawn from the
 counter-based generator Philox4x32-10 of Salmon, Moraes, Dror and Shaw,
 "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011), implemented from
 that definition:

@@ -29,10 +29,12 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_workspace_size",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_dropout",
+                                    "fa_bwd_workspace_size",
                                     "fa_decode", "fa_decode_num_splits",
                                     "fa_decode_workspace_size", "fa_fwd", "fa_fwd_bias",
-                                    "fa_fwd_f16", "fa_fwd_f32", "fa_status_string"]
+                                    "fa_fwd_dropout", "fa_fwd_f16", "fa_fwd_f32",
+                                    "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -221,6 +223,47 @@ def test_bias_entry_points_reject(bad, code):
 
 def test_bias_backward_checks_workspace():
     assert _bwd_bias(ws_bytes=8) == fa.FA_ERR_INVALID_ARG
+
+
+def _fwd_drop(p=0.1, **kw):
+    a = dict(B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125, causal=0, window=0, cu=None)
+    a.update(kw)
+    return fa.lib().fa_fwd_dropout(P[0], P[1], P[2], P[3], P[4], a["B"], a["Hq"], a["Hkv"],
+                                   a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                   a["window"], a["cu"], p, 1234, None)
+
+
+def _bwd_drop(p=0.1, ws_bytes=None, **kw):
+    a = dict(B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125, causal=0, window=0, cu=None)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_size(a["B"] * a["Nq"], a["Hq"], a["d"])
+    return fa.lib().fa_bwd_dropout(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8],
+                                   P[9], ws_bytes, a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                   a["Nk"], a["d"], a["scale"], a["causal"], a["window"],
+                                   a["cu"], p, 1234, None)
+
+
+BAD_DROPOUT = [
+    (dict(p=1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(p=1.5), fa.FA_ERR_INVALID_ARG),
+    (dict(p=-0.1), fa.FA_ERR_INVALID_ARG),
+    (dict(p=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
+    (dict(window=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(cu=ctypes.c_void_p(0x70002)), fa.FA_ERR_INVALID_ARG),  # misaligned cu_seqlens
+]
+
+
+@pytest.mark.parametrize("bad,code", BAD_DROPOUT)
+def test_dropout_entry_points_reject(bad, code):
+    assert _fwd_drop(**bad) == code
+    assert _bwd_drop(**bad) == code
+
+
+def test_dropout_backward_checks_workspace():
+    assert _bwd_drop(ws_bytes=8) == fa.FA_ERR_INVALID_ARG
 
 
 def test_status_strings():

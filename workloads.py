@@ -46,6 +46,10 @@ WORKLOADS = {
     "gqa_bias": dict(B=1, Hq=32, Hkv=8, N=8192, d=128, dtype="bf16", causal=False,
                      window=0, seed=7, bwd=True, bias_shape=(1, 1, "Q", "K"),
                      bias_masked=0.1),
+    # the GQA causal prefill with dropout p = 0.1 on the probabilities
+    # (seeded Philox keep-mask); forward and backward
+    "gqa_dropout": dict(B=1, Hq=32, Hkv=8, N=8192, d=128, dtype="bf16", causal=True,
+                        window=0, seed=8, bwd=True, dropout_p=0.1, dropout_seed=2024),
 }
 
 
