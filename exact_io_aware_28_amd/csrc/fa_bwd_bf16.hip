@@ -31,7 +31,8 @@
 //     dV = (P Z / (1 - p))^T dO,  dS = P (dP Z / (1 - p) - D),
 // and D = rowsum(dO * O) is unchanged, O being the dropped output.  The dQ
 // kernel (one query row per lane, runs of four keys) draws one Philox call
-// per four elements; the dK/dV kernel (one key per lane) one per element.
+// per four elements; so does the dK/dV kernel (one key per lane), whose
+// quads of lanes share each call through quad broadcasts.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -239,6 +240,27 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
         dp = mfma32(as_bf16x8(lds_read_b128_at(tdo, foff[st], ro)), vf[st], dp);
       }
 
+      // Dropout keep bits of this lane's key for the block's 16 rows.  The
+      // mask of one row and four consecutive keys is one Philox call, and
+      // the four lanes of a quad hold four consecutive keys and the same
+      // rows: lane t of the quad draws rows 8r + 4hl + t (r = 0..3), and
+      // quad broadcasts hand every lane its own key's bits.  kq[e] bit 4r:
+      // row 8r + 4hl + e of the block, key kj.
+      uint32_t kq[4] = {0u, 0u, 0u, 0u};
+      if constexpr (DROP) {
+        const int t = r32 & 3;
+        uint32_t mine = 0;  // bit 4r + u: row 8r + 4hl + t, key (kj & ~3) + u
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          mine |= keep4(kj & ~3, i0 + qb * 32 + 8 * r + 4 * hl + t, h_it, b, p.seed_lo,
+                        p.seed_hi, p.drop_thresh)
+                  << (4 * r);
+        kq[0] = quad_bcast<0>(mine) >> t;
+        kq[1] = quad_bcast<1>(mine) >> t;
+        kq[2] = quad_bcast<2>(mine) >> t;
+        kq[3] = quad_bcast<3>(mine) >> t;
+      }
+
       auto grads = [&](auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
@@ -257,8 +279,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
             if constexpr (DROP) {
               // O = (P Z / (1 - p)) V: dV takes the dropped, rescaled P and
               // the gradient reaching P is dP Z / (1 - p)
-              const bool kp = keep1(kj, i0 + qrow + e, h_it, b, p.seed_lo, p.seed_hi,
-                                    p.drop_thresh);
+              const bool kp = (kq[e] >> (4 * r)) & 1u;
               s[i] = kp ? pv * p.drop_scale : 0.f;
               dp[i] = pv * ((kp ? dp[i] * p.drop_scale : 0.f) - Dv[e]);
             } else {

@@ -324,14 +324,12 @@ __device__ __forceinline__ uint32_t keep4(int j4, int i, int h, int b, uint32_t 
          ((uint32_t)(w.z >= thresh) << 2) | ((uint32_t)(w.w >= thresh) << 3);
 }
 
-// Keep bit of the single element (i, j) of (b, h).
-__device__ __forceinline__ bool keep1(int j, int i, int h, int b, uint32_t seed_lo,
-                                      uint32_t seed_hi, uint32_t thresh) {
-  const uint4 w = philox4x32_10((uint32_t)j >> 2, (uint32_t)i, (uint32_t)h, (uint32_t)b,
-                                seed_lo, seed_hi);
-  const int e = j & 3;
-  const uint32_t x = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
-  return x >= thresh;
+// Value of x in lane (l & ~3) + E: a broadcast inside each quad of lanes
+// (DPP quad_perm, a VALU move).
+template <int E>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, E | (E << 2) | (E << 4) | (E << 6),
+                                               0xF, 0xF, false);
 }
 
 // Visibility of key j from query i (sequence-relative), delta = lk - lq.
