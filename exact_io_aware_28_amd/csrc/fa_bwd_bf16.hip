@@ -511,13 +511,11 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       // base + off with off = 8(i/4) + i%4
       const int base = j0 + kb * 32 + 4 * hl;
       const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
-      // dropout: keep bits of the four runs of four keys base + 8r + {0..3}
-      uint32_t keep = 0xFFFF;
+      // dropout: generator words of the four runs of four keys base + 8r + {0..3}
+      uint4 dw[4];
       if constexpr (DROP) {
-        keep = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          keep |= keep4(base + 8 * r, qi, h, b, p.seed_lo, p.seed_hi, p.drop_thresh) << (4 * r);
+        for (int r = 0; r < 4; ++r) dw[r] = drop_words(base + 8 * r, qi, h, b, p.seed_lo, p.seed_hi);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -530,7 +528,8 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
           pv = ok ? pv : 0.f;
         }
         if constexpr (DROP)
-          dp[i] = pv * ((((keep >> i) & 1) ? dp[i] * p.drop_scale : 0.f) - dq_d);
+          dp[i] = pv * ((word_of(dw[i >> 2], i & 3) >= p.drop_thresh ? dp[i] * p.drop_scale
+                                                                     : 0.f) - dq_d);
         else
           dp[i] = pv * (dp[i] - dq_d);
       }

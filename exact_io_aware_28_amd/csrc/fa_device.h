@@ -302,8 +302,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   for (int r = 0; r < 10; ++r) {
     const uint64_t a = (uint64_t)0xD2511F53u * c0;
     const uint64_t m = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(m >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(a >> 32) ^ c3 ^ k1;
+    // three-input XORs as one v_bitop3_b32 each (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(m >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(a >> 32), c3, k1, 0x96);
     c1 = (uint32_t)m;
     c3 = (uint32_t)a;
     c0 = n0;
@@ -314,12 +315,21 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return make_uint4(c0, c1, c2, c3);
 }
 
-// Keep bits of the dropout mask for keys j4 .. j4 + 3 (j4 % 4 == 0) of query
-// row i of (sequence b, query head h): bit e is set iff key j4 + e is kept.
+// Dropout words of keys j4 .. j4 + 3 (j4 % 4 == 0) of query row i of
+// (sequence b, query head h): key j4 + e is kept iff word e >= the threshold.
+__device__ __forceinline__ uint4 drop_words(int j4, int i, int h, int b, uint32_t seed_lo,
+                                            uint32_t seed_hi) {
+  return philox4x32_10((uint32_t)j4 >> 2, (uint32_t)i, (uint32_t)h, (uint32_t)b, seed_lo,
+                       seed_hi);
+}
+__device__ __forceinline__ uint32_t word_of(const uint4& w, int e) {  // e unrolled
+  return e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+}
+
+// The same as four keep bits: bit e is set iff key j4 + e is kept.
 __device__ __forceinline__ uint32_t keep4(int j4, int i, int h, int b, uint32_t seed_lo,
                                           uint32_t seed_hi, uint32_t thresh) {
-  const uint4 w = philox4x32_10((uint32_t)j4 >> 2, (uint32_t)i, (uint32_t)h, (uint32_t)b,
-                                seed_lo, seed_hi);
+  const uint4 w = drop_words(j4, i, h, b, seed_lo, seed_hi);
   return (uint32_t)(w.x >= thresh) | ((uint32_t)(w.y >= thresh) << 1) |
          ((uint32_t)(w.z >= thresh) << 2) | ((uint32_t)(w.w >= thresh) << 3);
 }

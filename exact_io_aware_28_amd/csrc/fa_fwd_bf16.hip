@@ -275,13 +275,13 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < NC; ++kc) {
         const int kb = kc >> 1, i0 = (kc & 1) * 8;
-        // dropout: keep bits of the chunk's two runs of four keys (the
+        // dropout: generator words of the chunk's two runs of four keys (the
         // normaliser l sums the undropped probabilities)
-        uint32_t keep = 0xFF;
-        if constexpr (DROP)
-          keep = keep4(key_of(kb, i0), qi, h, b, p.seed_lo, p.seed_hi, p.drop_thresh) |
-                 (keep4(key_of(kb, i0 + 4), qi, h, b, p.seed_lo, p.seed_hi, p.drop_thresh)
-                  << 4);
+        uint4 dw0, dw1;
+        if constexpr (DROP) {
+          dw0 = drop_words(key_of(kb, i0), qi, h, b, p.seed_lo, p.seed_hi);
+          dw1 = drop_words(key_of(kb, i0 + 4), qi, h, b, p.seed_lo, p.seed_hi);
+        }
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -293,7 +293,8 @@ void fwd_bf16_kernel(FwdParams p) {
             lsum1 += pv[e];
           else
             lsum0 += pv[e];
-          if constexpr (DROP) pv[e] = ((keep >> e) & 1) ? pv[e] : 0.f;
+          if constexpr (DROP)
+            pv[e] = word_of(e < 4 ? dw0 : dw1, e & 3) >= p.drop_thresh ? pv[e] : 0.f;
         }
         const bf16x8 pb = pack8_t<F16>(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         bf16x8 va[DB];
