@@ -235,7 +235,9 @@ void decode_split_kernel(DecodeParams p) {
 }
 
 // One wave per (sequence b, position i, head h); lane owns D/64 consecutive
-// output columns.
+// output columns.  The split logsumexps are read in parallel (lane s holds
+// split s, 64 at a time) and reduced across the wave; the partial outputs
+// are then accumulated four splits at a time so that their loads overlap.
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(DecodeParams p) {
   constexpr int kPer = D / 64;
@@ -246,25 +248,52 @@ __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(DecodeParam
   const int i = (int)(bi % p.Nq);
   const int b = (int)(bi / p.Nq);
   const int lane = threadIdx.x;
+  const int ns = p.num_splits;
   const int64_t lstride = (int64_t)p.B * p.Hq * p.Nq;         // one split of lpart
   const int64_t ostride = (int64_t)p.B * p.Nq * p.Hq * D;     // one split of opart
   const float* lp = p.lpart + ((int64_t)b * p.Hq + h) * p.Nq + i;
   const float* opp = p.opart + row * D + lane * kPer;
 
+  // maximum of the split logsumexps
   float mx = -kInf;
-  for (int s = 0; s < p.num_splits; ++s) mx = fmaxf(mx, lp[s * lstride]);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) mx = fmaxf(mx, lp[(int64_t)(s0 + lane) * lstride]);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+
   float o[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) o[e] = 0.f;
   float sum = 0.f;
   if (mx != -kInf) {
-    for (int s = 0; s < p.num_splits; ++s) {
-      const float ls = lp[s * lstride];
-      if (ls == -kInf) continue;
-      const float w = expf(ls - mx);
-      sum += w;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      // weight of split s0 + lane (0 for an empty split or past the end)
+      const float ls = (s0 + lane < ns) ? lp[(int64_t)(s0 + lane) * lstride] : -kInf;
+      const float w = (ls == -kInf) ? 0.f : expf(ls - mx);
+      float ws = w;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) o[e] = fmaf(w, opp[s * ostride + e], o[e]);
+      for (int m = 32; m > 0; m >>= 1) ws += __shfl_xor(ws, m, 64);
+      sum += ws;
+      const int n = min(64, ns - s0);
+      int k = 0;
+      for (; k + 4 <= n; k += 4) {
+        float wk[4], v[4][kPer];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wk[u] = __shfl(w, k + u, 64);
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) v[u][e] = opp[(int64_t)(s0 + k + u) * ostride + e];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) o[e] = fmaf(wk[u], v[u][e], o[e]);
+      }
+      for (; k < n; ++k) {
+        const float wk = __shfl(w, k, 64);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) o[e] = fmaf(wk, opp[(int64_t)(s0 + k) * ostride + e], o[e]);
+      }
     }
   }
   const float inv = (sum > 0.f) ? 1.0f / sum : 0.f;

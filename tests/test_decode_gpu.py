@@ -81,6 +81,7 @@ CASES = [
     (1, 32, 4, 9, 777, 128, [777], True, 0, 1),              # 72 rows: three row blocks
     (2, 8, 2, 1, 300, 128, [300, 64], True, 0, 50),          # more splits than tiles
     (3, 8, 1, 4, 520, 64, [520, 31, 33], True, 100, 4),      # MQA, window, ragged ends
+    (2, 8, 2, 2, 5000, 128, [5000, 3100], True, 0, 130),    # > 64 splits: chunked merge
 ]
 
 
