@@ -38,6 +38,9 @@ int check_common(const void* const* tensors, int ntensors, const float* const* s
   const int64_t tiles = (int64_t)B * Hq * ((Nq + qtile_rows - 1) / qtile_rows);
   if (tiles > (int64_t)UINT32_MAX / 2) return FA_ERR_UNSUPPORTED;
   if ((int64_t)B * Nq * Hq > (int64_t)INT32_MAX * 64) return FA_ERR_UNSUPPORTED;
+  // a staged tile (64 rows of one head) must span less than 4 GiB of its
+  // tensor: the buffer descriptors that bound it count bytes in 32 bits
+  if ((int64_t)Hq * d * 2 * 64 >= ((int64_t)1 << 32)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

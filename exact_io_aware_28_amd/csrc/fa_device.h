@@ -222,10 +222,12 @@ struct TileDma {
     }
   }
   // Stage rows [j0, j0 + ROWS) of a tensor whose row 0 is at `g`; rows at or
-  // past `limit` read as zero.
+  // past `limit` read as zero.  The descriptor spans at most the tile's own
+  // rows, so its 32-bit byte range cannot wrap however far `limit` lies
+  // beyond the tile (a tensor can exceed 4 GiB).
   __device__ __forceinline__ void issue(const __bf16* g, uint32_t stride_bytes, int j0,
                                         int limit, __bf16* lds) const {
-    const int valid = limit - j0;  // >= 1 inside the loops that call this
+    const int valid = min(limit - j0, ROWS);  // >= 1 inside the loops that call this
     const uint32_t nbytes = (uint32_t)(valid - 1) * stride_bytes + (uint32_t)D * 2u;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(g + (int64_t)j0 * (stride_bytes / 2), nbytes);
 #pragma unroll

@@ -88,7 +88,9 @@ typedef enum fa_status {
  * Pointers q, k, v, o must be 16-byte aligned; lse 4-byte aligned.
  * Returns FA_ERR_INVALID_ARG for a null or misaligned pointer, a size < 1,
  * Hq % Hkv != 0, a non-finite scale, causal not in {0,1}, window < 0;
- * FA_ERR_UNSUPPORTED for d not in {64, 128}, or packed with Nq != Nk.
+ * FA_ERR_UNSUPPORTED for d not in {64, 128}, packed with Nq != Nk, or
+ * Hq * d * 128 >= 2^32 (64 token rows of one tensor must span less than
+ * 4 GiB; tensors themselves may be larger).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nk, int d,

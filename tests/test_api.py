@@ -91,6 +91,9 @@ BAD_FWD = [
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(cu=P[5], Nq=64, Nk=128), fa.FA_ERR_UNSUPPORTED),
     (dict(cu=ctypes.c_void_p(0x10001)), fa.FA_ERR_INVALID_ARG),
+    # 64 rows of one head would span 4 GiB: beyond the 32-bit tile descriptors
+    (dict(Hq=262144, Hkv=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=262144 * 2, Hkv=2, d=64), fa.FA_ERR_UNSUPPORTED),
 ]
 
 
