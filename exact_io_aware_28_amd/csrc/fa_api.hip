@@ -76,12 +76,13 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
   return p;
 }
 
-// Dropout probability in [0, 1): integer threshold floor(p * 2^32) (a key
-// is dropped iff its 32-bit Philox word is below it) and the scale 1/(1-p).
+// Dropout probability in [0, 1): 16-bit threshold T = floor(p * 2^16) (a
+// key is dropped iff its 16-bit Philox slot is below it) and the scale
+// 2^16 / (2^16 - T), the inverse of the exact keep probability.
 int check_dropout(float dropout_p, uint32_t* thresh, float* scale) {
   if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;  // also NaN
-  *thresh = (uint32_t)((double)dropout_p * 4294967296.0);
-  *scale = (float)(1.0 / (1.0 - (double)dropout_p));
+  *thresh = (uint32_t)((double)dropout_p * 65536.0);
+  *scale = (float)(65536.0 / (65536.0 - (double)*thresh));
   return FA_OK;
 }
 

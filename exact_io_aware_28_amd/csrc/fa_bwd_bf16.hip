@@ -31,8 +31,9 @@
 //     dV = (P Z / (1 - p))^T dO,  dS = P (dP Z / (1 - p) - D),
 // and D = rowsum(dO * O) is unchanged, O being the dropped output.  The dQ
 // kernel (one query row per lane, runs of four keys) draws one Philox call
-// per four elements; so does the dK/dV kernel (one key per lane), whose
-// quads of lanes share each call through quad broadcasts.
+// per eight elements (16-bit slots); the dK/dV kernel (one key per lane)
+// one per four, its quads of lanes sharing each call through quad
+// broadcasts.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -511,11 +512,13 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       // base + off with off = 8(i/4) + i%4
       const int base = j0 + kb * 32 + 4 * hl;
       const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
-      // dropout: generator words of the four runs of four keys base + 8r + {0..3}
-      uint4 dw[4];
+      // dropout: two generator calls cover the half's 16 keys of this lane,
+      // base + 16c + 8a + {0..3}: element i takes slot i & 7 of call i >> 3
+      uint4 dw[2];
       if constexpr (DROP) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dw[r] = drop_words(base + 8 * r, qi, h, b, p.seed_lo, p.seed_hi);
+        for (int c2 = 0; c2 < 2; ++c2)
+          dw[c2] = drop_call(base + 16 * c2, qi, h, b, p.seed_lo, p.seed_hi);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -528,7 +531,7 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
           pv = ok ? pv : 0.f;
         }
         if constexpr (DROP)
-          dp[i] = pv * ((word_of(dw[i >> 2], i & 3) >= p.drop_thresh ? dp[i] * p.drop_scale
+          dp[i] = pv * ((slot_of(dw[i >> 3], i & 7) >= p.drop_thresh ? dp[i] * p.drop_scale
                                                                      : 0.f) - dq_d);
         else
           dp[i] = pv * (dp[i] - dq_d);

@@ -317,23 +317,33 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return make_uint4(c0, c1, c2, c3);
 }
 
-// Dropout words of keys j4 .. j4 + 3 (j4 % 4 == 0) of query row i of
-// (sequence b, query head h): key j4 + e is kept iff word e >= the threshold.
-__device__ __forceinline__ uint4 drop_words(int j4, int i, int h, int b, uint32_t seed_lo,
-                                            uint32_t seed_hi) {
-  return philox4x32_10((uint32_t)j4 >> 2, (uint32_t)i, (uint32_t)h, (uint32_t)b, seed_lo,
-                       seed_hi);
+// Dropout generator call shared by the keys 16m + 4t + {0..3, 8..11} of
+// query row i of (sequence b, query head h), for any such key j
+// (m = j >> 4, t = (j >> 2) & 1): counter (2m + t, i, h, b).  Key j takes
+// slot s = 4 ((j >> 3) & 1) + (j & 3): the 16-bit half s & 1 (0 low) of
+// output word s >> 1, and is kept iff that half >= the 16-bit threshold.
+__device__ __forceinline__ uint4 drop_call(int j, int i, int h, int b, uint32_t seed_lo,
+                                           uint32_t seed_hi) {
+  const uint32_t c0 = 2u * ((uint32_t)j >> 4) + (((uint32_t)j >> 2) & 1u);
+  return philox4x32_10(c0, (uint32_t)i, (uint32_t)h, (uint32_t)b, seed_lo, seed_hi);
 }
 __device__ __forceinline__ uint32_t word_of(const uint4& w, int e) {  // e unrolled
   return e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
 }
+__device__ __forceinline__ uint32_t slot_of(const uint4& w, int s) {  // s unrolled, 0..7
+  const uint32_t x = word_of(w, s >> 1);
+  return (s & 1) ? (x >> 16) : (x & 0xFFFFu);
+}
 
-// The same as four keep bits: bit e is set iff key j4 + e is kept.
+// Keep bits of keys j4 .. j4 + 3 (j4 % 4 == 0) of query row i: bit e is set
+// iff key j4 + e is kept (slots 4a .. 4a + 3, a = (j4 >> 3) & 1).
 __device__ __forceinline__ uint32_t keep4(int j4, int i, int h, int b, uint32_t seed_lo,
                                           uint32_t seed_hi, uint32_t thresh) {
-  const uint4 w = drop_words(j4, i, h, b, seed_lo, seed_hi);
-  return (uint32_t)(w.x >= thresh) | ((uint32_t)(w.y >= thresh) << 1) |
-         ((uint32_t)(w.z >= thresh) << 2) | ((uint32_t)(w.w >= thresh) << 3);
+  const uint4 w = drop_call(j4, i, h, b, seed_lo, seed_hi);
+  const bool a = (j4 >> 3) & 1;
+  const uint32_t lo = a ? w.z : w.x, hi = a ? w.w : w.y;
+  return (uint32_t)((lo & 0xFFFFu) >= thresh) | ((uint32_t)((lo >> 16) >= thresh) << 1) |
+         ((uint32_t)((hi & 0xFFFFu) >= thresh) << 2) | ((uint32_t)((hi >> 16) >= thresh) << 3);
 }
 
 // Value of x in lane (l & ~3) + E: a broadcast inside each quad of lanes

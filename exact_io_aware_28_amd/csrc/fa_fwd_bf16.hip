@@ -38,8 +38,9 @@
 //     unchanged.  The other wave of the SIMD covers the load latency.
 //   * Optional dropout on the probabilities (inferensys.com glossary
 //     "FlashAttention", the paragraph on the one fused kernel: matrix
-//     multiply, softmax, dropout and masking): a Philox4x32-10 call per run
-//     of four keys gives the keep bits; dropped probabilities still count
+//     multiply, softmax, dropout and masking): a Philox4x32-10 call per
+//     16-key chunk and lane gives the keep bits of the lane's eight keys
+//     (16-bit slots); dropped probabilities still count
 //     in l (the softmax is of the undropped scores), the kept ones go to the
 //     P V product and 1 / (1 - p) is folded into the final division by l.
 //   * Lazy rescaling: the running maximum used for exponentiation is only
@@ -275,13 +276,10 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < NC; ++kc) {
         const int kb = kc >> 1, i0 = (kc & 1) * 8;
-        // dropout: generator words of the chunk's two runs of four keys (the
-        // normaliser l sums the undropped probabilities)
-        uint4 dw0, dw1;
-        if constexpr (DROP) {
-          dw0 = drop_words(key_of(kb, i0), qi, h, b, p.seed_lo, p.seed_hi);
-          dw1 = drop_words(key_of(kb, i0 + 4), qi, h, b, p.seed_lo, p.seed_hi);
-        }
+        // dropout: one generator call covers the chunk's eight keys, slot e
+        // for pv[e] (the normaliser l sums the undropped probabilities)
+        uint4 dw;
+        if constexpr (DROP) dw = drop_call(key_of(kb, i0), qi, h, b, p.seed_lo, p.seed_hi);
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -293,8 +291,7 @@ void fwd_bf16_kernel(FwdParams p) {
             lsum1 += pv[e];
           else
             lsum0 += pv[e];
-          if constexpr (DROP)
-            pv[e] = word_of(e < 4 ? dw0 : dw1, e & 3) >= p.drop_thresh ? pv[e] : 0.f;
+          if constexpr (DROP) pv[e] = slot_of(dw, e) >= p.drop_thresh ? pv[e] : 0.f;
         }
         const bf16x8 pb = pack8_t<F16>(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         bf16x8 va[DB];

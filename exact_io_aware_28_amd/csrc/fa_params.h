@@ -28,11 +28,11 @@ struct FwdParams {
   const float* bias;
   int64_t bias_sb, bias_sh, bias_sq;
   int bias_vec4;              // every row start is 16-byte aligned
-  // dropout on the probabilities: element (b, h, i, j) is kept iff word j % 4
-  // of Philox4x32-10 at counter (j / 4, i, h, b), key (seed_lo, seed_hi), is
-  // >= drop_thresh; kept values are multiplied by drop_scale = 1 / (1 - p)
+  // dropout on the probabilities: element (b, h, i, j) is kept iff its 16-bit
+  // slot of Philox4x32-10 (drop_call in fa_device.h), key (seed_lo,
+  // seed_hi), is >= drop_thresh; kept values are multiplied by drop_scale
   int dropout;                // 0: no dropout (the other fields are unused)
-  uint32_t drop_thresh;       // floor(p * 2^32)
+  uint32_t drop_thresh;       // floor(p * 2^16)
   uint32_t seed_lo, seed_hi;
   float drop_scale;
 };

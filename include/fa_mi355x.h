@@ -188,18 +188,23 @@ int fa_bwd_bias(const void* q, const void* k, const void* v, const void* o,
 /*
  * Forward and backward with dropout on the attention probabilities
  * (inferensys.com glossary "FlashAttention", the paragraph on the single
- * fused kernel, lists dropout among the operations fused into one pass).  O = (P * Z / (1 - dropout_p)) V, where P is the
- * softmax of fa_fwd and Z is a 0/1 keep-mask; LSE is that of the undropped P
- * (as fa_fwd), so fa_bwd_dropout rebuilds P from it and regenerates Z
- * instead of storing it.  Gradients: dV = (P Z / (1 - p))^T dO,
+ * fused kernel, lists dropout among the operations fused into one pass).
+ * O = (P * Z / (1 - p)) V, where P is the softmax of fa_fwd and Z is a 0/1
+ * keep-mask; LSE is that of the undropped P (as fa_fwd), so fa_bwd_dropout
+ * rebuilds P from it and regenerates Z instead of storing it.  Gradients: dV = (P Z / (1 - p))^T dO,
  * dP = (dO V^T) Z / (1 - p), D_i = sum_c dO_ic O_ic, dS = P (dP - D).
  * The pages fix no random number generator; this library's mask is:
  *   element (b, h, i, j) -- batch entry or packed sequence b, query head h,
- *   query row i and key j counted from the start of the sequence -- is kept
- *   iff word (j mod 4) of Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
- *   "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) at counter
- *   (floor(j / 4), i, h, b) with key (seed mod 2^32, floor(seed / 2^32)) is
- *   >= floor(dropout_p * 2^32), dropout_p taken as a double.
+ *   query row i and key j counted from the start of the sequence -- reads
+ *   Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+ *   As Easy as 1, 2, 3", SC 2011) at counter
+ *   (2 floor(j / 16) + (floor(j / 4) mod 2), i, h, b) with key
+ *   (seed mod 2^32, floor(seed / 2^32)); with s = 4 (floor(j / 8) mod 2) +
+ *   (j mod 4), its 16-bit slot is half (s mod 2) (0 = low) of output word
+ *   floor(s / 2).  The key is kept iff the slot >= T = floor(p * 2^16), p
+ *   being dropout_p widened to double, and kept probabilities are scaled by
+ *   2^16 / (2^16 - T), the inverse of the exact keep probability (the
+ *   1 / (1 - p) of the formulas above).
  * The same seed and dropout_p must be passed to the forward and the
  * backward.  dropout_p = 0 gives exactly fa_fwd / fa_bwd.  Other arguments,
  * layouts and errors as fa_fwd and fa_bwd (dense or packed batches), plus

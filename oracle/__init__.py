@@ -20,4 +20,4 @@ from .attention import (  # noqa: F401
     sequence_spans,
 )
 from .online_recurrence import online_attention  # noqa: F401
-from .philox import drop_threshold, keep_mask, philox4x32_10  # noqa: F401
+from .philox import drop_threshold, keep_mask, keep_scale, philox4x32_10  # noqa: F401

@@ -55,7 +55,7 @@ Layouts (token-major, d innermost):
 
 import numpy as np
 
-from .philox import keep_mask
+from .philox import keep_mask, keep_scale
 
 
 def kv_head_of(h, hq, hkv):
@@ -105,10 +105,12 @@ def _softmax_rows(s):
 
 
 def _dropped(p, keep, p_drop):
-    """P * Z / (1 - p_drop): the probabilities that multiply V."""
+    """P * Z / (1 - p_drop): the probabilities that multiply V, with p_drop
+    taken as the exact drop probability of the mask (p rounded down to a
+    multiple of 2^-16, oracle/philox.py)."""
     if keep is None:
         return p
-    return np.where(keep, p / (1.0 - p_drop), 0.0)
+    return np.where(keep, p * keep_scale(p_drop), 0.0)
 
 
 def _head_fwd(q, k, v, scale, ok, bias=None, keep=None, p_drop=0.0):

@@ -18,14 +18,21 @@ that definition:
   constants (k0 += 0x9E3779B9, k1 += 0xBB67AE85, modulo 2^32).
 
 Dropout element (b, h, i, j) -- batch entry or packed sequence b, query head
-h, query row i (inside its sequence), key j -- uses
+h, query row i (inside its sequence), key j -- takes one 16-bit slot of a
+call; one call serves eight keys of a row:
 
-  counter = (j >> 2, i, h, b),  key = (seed mod 2^32, seed >> 32)
+  counter = (2 * (j >> 4) + ((j >> 2) & 1), i, h, b),
+  key     = (seed mod 2^32, seed >> 32),
+  slot    = 4 * ((j >> 3) & 1) + (j & 3)   (0..7),
+  u       = 16-bit half (slot & 1: 0 low, 1 high) of output word slot >> 1.
 
-and output word j & 3 of that call, u.  The key is kept iff
-u >= floor(p * 2^32) (p in [0, 1)), and kept probabilities are scaled by
-1 / (1 - p).  Pinned by the generator's published known-answer vectors and by
-the statistics of the mask (tests/oracle_pins.py).
+So the keys 16m + 4t + {0, 1, 2, 3, 8, 9, 10, 11} (t = 0, 1) share a call.
+With T = floor(p * 2^16) (p in [0, 1)), a key is kept iff u >= T; the keep
+probability is then exactly 1 - T / 2^16, and kept probabilities are scaled
+by 2^16 / (2^16 - T), its inverse (1 / (1 - p) up to p's rounding to
+multiples of 2^-16), so that the dropped output stays unbiased.  Pinned by
+the generator's published known-answer vectors and by the statistics of the
+mask (tests/oracle_pins.py).
 """
 
 import numpy as np
@@ -55,18 +62,33 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def drop_threshold(p):
-    """Integer threshold floor(p * 2^32): a key is dropped iff its word < it."""
+    """16-bit threshold T = floor(p * 2^16): a key is dropped iff its slot < T."""
     if not 0.0 <= p < 1.0:
         raise ValueError("dropout probability must be in [0, 1)")
-    return int(p * 4294967296.0)
+    return int(p * 65536.0)
+
+
+def keep_scale(p):
+    """Scale of the kept probabilities, 2^16 / (2^16 - T): the inverse of the
+    exact keep probability."""
+    return 65536.0 / (65536.0 - drop_threshold(p))
+
+
+def slot_words(j):
+    """(counter word c0, output word, half) of key j, as integer arrays."""
+    j = np.asarray(j, dtype=np.int64)
+    c0 = 2 * (j >> 4) + ((j >> 2) & 1)
+    slot = 4 * ((j >> 3) & 1) + (j & 3)
+    return c0, slot >> 1, slot & 1
 
 
 def keep_mask(seed, b, h, rows, nk, p):
     """Boolean [len(rows), nk]: which keys query rows `rows` of (b, h) keep."""
     rows = np.asarray(rows, dtype=np.int64)
-    j = np.arange(nk, dtype=np.int64)
-    words = philox4x32_10(j[None, :] >> 2, rows[:, None], h, b,
+    c0, word, half = slot_words(np.arange(nk, dtype=np.int64))
+    words = philox4x32_10(c0[None, :], rows[:, None], h, b,
                           seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    e = (j & 3)[None, :]
-    u = np.select([e == 0, e == 1, e == 2, e == 3], words)
-    return u >= np.uint64(drop_threshold(p))
+    w = word[None, :]
+    u = np.select([w == 0, w == 1, w == 2, w == 3], words)
+    u16 = (u >> (np.uint64(16) * half[None, :].astype(np.uint64))) & np.uint64(0xFFFF)
+    return u16 >= np.uint64(drop_threshold(p))

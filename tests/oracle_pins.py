@@ -510,7 +510,7 @@ def check_dropout_mask_statistics(A):
                   philox.keep_mask(8, 0, 0, np.arange(64), 64, 0.5),
                   philox.keep_mask(7 + (1 << 32), 0, 0, np.arange(64), 64, 0.5)):
         assert 0.3 < (a != other).mean() < 0.7
-    # keys 4t .. 4t+3 come from different words: not all equal within groups
+    # keys 4t .. 4t+3 take different slots of a call: not all equal within groups
     g = a.reshape(64, 16, 4)
     assert (g != g[..., :1]).any(axis=2).mean() > 0.5
     # rows restricted to a subset agree with the full mask
@@ -532,11 +532,12 @@ def _torch_dropout_reference(q, k, v, scale, causal, keep, p):
 def check_dropout_matches_masked_softmax(A):
     """Forward with dropout equals torch's softmax times the keep-mask over
     1 - p, times V; LSE is that of the undropped scores; p = 0 (or a p whose
-    threshold is 0) is plain attention."""
+    threshold is 0) is plain attention.  The p here are multiples of 2^-16,
+    for which 1 / (1 - p) is exactly the mask's scale."""
     from oracle import philox
     rng = _rng(45)
     q, k, v = _dense(rng, 2, 13, 18, 4, 2, 8)
-    for causal, p in [(False, 0.3), (True, 0.6)]:
+    for causal, p in [(False, 0.3125), (True, 0.625)]:
         o, lse = A.attn_fwd(q, k, v, 0.5, causal, dropout_p=p, seed=99)
         _, lse0 = A.attn_fwd(q, k, v, 0.5, causal)
         assert np.allclose(lse, lse0, atol=1e-12)
@@ -553,7 +554,9 @@ def check_dropout_matches_masked_softmax(A):
 
 def check_dropout_unbiased(A):
     """Averaged over many seeds the dropped output approaches the plain one
-    (E[Z] / (1 - p) = 1), within five standard errors."""
+    (E[Z] times the scale is 1), within five standard errors; p = 0.4 is not
+    a multiple of 2^-16, so this also pins the scale to the mask's exact keep
+    probability."""
     rng = _rng(46)
     q, k, v = _dense(rng, 1, 6, 9, 1, 1, 4)
     o0, _ = A.attn_fwd(q, k, v, 0.7)
@@ -570,7 +573,7 @@ def check_dropout_backward(A):
     rng = _rng(47)
     q, k, v = _dense(rng, 1, 10, 14, 2, 1, 6)
     do = rng.standard_normal(q.shape)
-    p = 0.35
+    p = 0.375
     dq, dk, dv = A.attn_bwd(q, k, v, do, 0.6, True, dropout_p=p, seed=11)
     tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
     loss = 0

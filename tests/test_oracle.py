@@ -142,12 +142,15 @@ def _keep_rows_keys_swapped(dropout_p, seed, b, h, rows, nk):
     if dropout_p == 0.0:
         return None
     from oracle import philox
-    rows = np.asarray(rows)
-    j = np.arange(nk)
-    w = philox.philox4x32_10(rows[:, None] >> 2, j[None, :], h, b, seed & 0xFFFFFFFF, seed >> 32)
-    e = (rows & 3)[:, None]
-    u = np.select([e == 0, e == 1, e == 2, e == 3], w)
-    return u >= np.uint64(philox.drop_threshold(dropout_p))
+    rows = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(nk)[None, :]
+    c0 = 2 * (rows >> 4) + ((rows >> 2) & 1)
+    slot = 4 * ((rows >> 3) & 1) + (rows & 3)
+    w = philox.philox4x32_10(c0, j, h, b, seed & 0xFFFFFFFF, seed >> 32)
+    word = slot >> 1
+    u = np.select([word == 0, word == 1, word == 2, word == 3], w)
+    u16 = (u >> (np.uint64(16) * (slot & 1).astype(np.uint64))) & np.uint64(0xFFFF)
+    return u16 >= np.uint64(philox.drop_threshold(dropout_p))
 
 
 def _head_bwd_dropout_dp_unmasked(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
