@@ -31,9 +31,9 @@
 //     dV = (P Z / (1 - p))^T dO,  dS = P (dP Z / (1 - p) - D),
 // and D = rowsum(dO * O) is unchanged, O being the dropped output.  The dQ
 // kernel (one query row per lane, runs of four keys) draws one Philox call
-// per eight elements (16-bit slots); the dK/dV kernel (one key per lane)
-// one per four, its quads of lanes sharing each call through quad
-// broadcasts.
+// per eight elements (16-bit slots); so does the dK/dV kernel (one key per
+// lane), whose lanes with keys in the same group of eight share each call
+// through quad broadcasts and a row rotation.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -84,6 +84,22 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ 2. dK, dV
+// Eight dropout keep bits of one row (bit s: slot s of the generator call of
+// key j's group, drop_call in fa_device.h).
+__device__ __forceinline__ uint32_t keep8(int j, int i, int h, int b, uint32_t seed_lo,
+                                          uint32_t seed_hi, uint32_t thresh) {
+  const uint4 w = drop_call(j, i, h, b, seed_lo, seed_hi);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) bits |= (uint32_t)(slot_of(w, s2) >= thresh) << s2;
+  return bits;
+}
+
+// Value of x in lane l ^ 8 (DPP row_ror:8 inside each row of 16 lanes).
+__device__ __forceinline__ uint32_t row_ror8(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+}
+
 // dK and dV accumulators plus the resident K and V fragments take about 350
 // registers at d = 128 (one wave per SIMD); d = 64 fits two waves.
 template <int D>
@@ -241,25 +257,32 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
         dp = mfma32(as_bf16x8(lds_read_b128_at(tdo, foff[st], ro)), vf[st], dp);
       }
 
-      // Dropout keep bits of this lane's key for the block's 16 rows.  The
-      // mask of one row and four consecutive keys is one Philox call, and
-      // the four lanes of a quad hold four consecutive keys and the same
-      // rows: lane t of the quad draws rows 8r + 4hl + t (r = 0..3), and
-      // quad broadcasts hand every lane its own key's bits.  kq[e] bit 4r:
-      // row 8r + 4hl + e of the block, key kj.
-      uint32_t kq[4] = {0u, 0u, 0u, 0u};
+      // Dropout keep bits of this lane's key for the block's 16 rows.  One
+      // Philox call gives a row's bits for the eight keys 16m + 4t +
+      // {0..3, 8..11}, held by the eight lanes l with equal bits 2 and 4 (a
+      // quad and the quad eight lanes away).  Group lane u = 4a + t (a = bit 3
+      // of the lane, t = its low bits) draws block rows rho = 2u and 2u + 1
+      // (rho = 4r + e is row 8r + 4hl + e), and quad broadcasts plus one row
+      // rotation hand every lane all eight drawn words.  kw[u]: group lane
+      // u's word, shifted so that bit 8 (rho & 1) is this lane's key.
+      uint32_t kw[8];
       if constexpr (DROP) {
-        const int t = r32 & 3;
-        uint32_t mine = 0;  // bit 4r + u: row 8r + 4hl + t, key (kj & ~3) + u
+        const int t = r32 & 3, a = (r32 >> 3) & 1, u = 4 * a + t;
+        uint32_t mine = 0;  // bit 8 (rho & 1) + s: row rho, slot s
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          mine |= keep4(kj & ~3, i0 + qb * 32 + 8 * r + 4 * hl + t, h_it, b, p.seed_lo,
-                        p.seed_hi, p.drop_thresh)
-                  << (4 * r);
-        kq[0] = quad_bcast<0>(mine) >> t;
-        kq[1] = quad_bcast<1>(mine) >> t;
-        kq[2] = quad_bcast<2>(mine) >> t;
-        kq[3] = quad_bcast<3>(mine) >> t;
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int rho = 2 * u + k2;
+          const int row = i0 + qb * 32 + 8 * (rho >> 2) + 4 * hl + (rho & 3);
+          mine |= keep8(kj, row, h_it, b, p.seed_lo, p.seed_hi, p.drop_thresh) << (8 * k2);
+        }
+        const uint32_t other = row_ror8(mine);  // the quad eight lanes away
+        const uint32_t own_w[4] = {quad_bcast<0>(mine), quad_bcast<1>(mine),
+                                   quad_bcast<2>(mine), quad_bcast<3>(mine)};
+        const uint32_t oth_w[4] = {quad_bcast<0>(other), quad_bcast<1>(other),
+                                   quad_bcast<2>(other), quad_bcast<3>(other)};
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          kw[v] = (((v >> 2) == a) ? own_w[v & 3] : oth_w[v & 3]) >> u;
       }
 
       auto grads = [&](auto masked_tag) {
@@ -280,7 +303,8 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
             if constexpr (DROP) {
               // O = (P Z / (1 - p)) V: dV takes the dropped, rescaled P and
               // the gradient reaching P is dP Z / (1 - p)
-              const bool kp = (kq[e] >> (4 * r)) & 1u;
+              // row rho = i = 4r + e was drawn by group lane i >> 1
+              const bool kp = (kw[i >> 1] >> (8 * (i & 1))) & 1u;
               s[i] = kp ? pv * p.drop_scale : 0.f;
               dp[i] = pv * ((kp ? dp[i] * p.drop_scale : 0.f) - Dv[e]);
             } else {

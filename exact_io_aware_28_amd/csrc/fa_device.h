@@ -335,17 +335,6 @@ __device__ __forceinline__ uint32_t slot_of(const uint4& w, int s) {  // s unrol
   return (s & 1) ? (x >> 16) : (x & 0xFFFFu);
 }
 
-// Keep bits of keys j4 .. j4 + 3 (j4 % 4 == 0) of query row i: bit e is set
-// iff key j4 + e is kept (slots 4a .. 4a + 3, a = (j4 >> 3) & 1).
-__device__ __forceinline__ uint32_t keep4(int j4, int i, int h, int b, uint32_t seed_lo,
-                                          uint32_t seed_hi, uint32_t thresh) {
-  const uint4 w = drop_call(j4, i, h, b, seed_lo, seed_hi);
-  const bool a = (j4 >> 3) & 1;
-  const uint32_t lo = a ? w.z : w.x, hi = a ? w.w : w.y;
-  return (uint32_t)((lo & 0xFFFFu) >= thresh) | ((uint32_t)((lo >> 16) >= thresh) << 1) |
-         ((uint32_t)((hi & 0xFFFFu) >= thresh) << 2) | ((uint32_t)((hi >> 16) >= thresh) << 3);
-}
-
 // Value of x in lane (l & ~3) + E: a broadcast inside each quad of lanes
 // (DPP quad_perm, a VALU move).
 template <int E>
