@@ -34,7 +34,10 @@ import workloads  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attention TFLOP/s + % of bf16 MFMA peak, causal fwd N=8192 d=128 GQA"
-FWD_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h", "fa_params.h"]
+# the forward kernel's sources and the build script that sets its code-generation
+# options (paths relative to the package's csrc/)
+FWD_SOURCES = ["fa_fwd_kernel.h", "fa_fwd_bf16.hip", "fa_fwd_bf16_d128.hip", "fa_device.h",
+               "fa_params.h", "../build.py"]
 
 
 def attention_flops(inp):

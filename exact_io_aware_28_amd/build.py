@@ -31,13 +31,22 @@ CFLAGS = [
 ]
 
 
+# Per-file code-generation options: the d = 128 forward kernels without a
+# bias schedule better with the max-ILP strategy (measured 1-3 % faster);
+# the other kernels are slower with it.
+PER_FILE_FLAGS = {
+    "fa_fwd_bf16_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)

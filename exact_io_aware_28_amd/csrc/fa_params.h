@@ -86,6 +86,8 @@ struct DecodeParams {
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
+// d = 128 forward without a bias (bf16 or fp16): fa_fwd_bf16_d128.hip
+hipError_t launch_fwd_d128(const FwdParams& p, hipStream_t stream, bool f16);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
