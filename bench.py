@@ -141,7 +141,47 @@ def device_inputs(inp):
     return out
 
 
-def time_forward(inp, dev, steps, warmup):
+# The GPU clock ramps up over the first ~100 ms of sustained work: a few
+# warm-up launches leave the timed region partly at a low clock.  Warm-up
+# therefore runs at least --warmup launches and at least this long.
+MIN_WARMUP_MS = 300.0
+
+
+def warm_up(launch, warmup, min_ms=MIN_WARMUP_MS):
+    """Run `warmup` launches, then more in batches of 10 until `min_ms` of
+    wall time has passed; returns the number of launches."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(warmup):
+        launch()
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(10):
+            launch()
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def timed(launch, steps, stream):
+    """Time exactly `steps` launches with HIP events on `stream`: one event
+    before the first and one after each launch.  Returns (ms per launch over
+    the whole region, per-launch ms)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        launch()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[-1]) / steps, per
+
+
+def time_forward(inp, dev, steps, warmup, stats=None):
     import torch
     import exact_io_aware_28_amd as fa
     fn = {"bf16": fa.fa_fwd, "f16": fa.fa_fwd_f16, "f32": fa.fa_fwd_f32}[inp["dtype"]]
@@ -155,17 +195,16 @@ def time_forward(inp, dev, steps, warmup):
         dp, ds = inp["dropout_p"], inp["dropout_seed"]
         fn = lambda q, k, v, **a: fa.fa_fwd_dropout(q, k, v, dp, ds, **a)
     o, lse = fn(dev["q"], dev["k"], dev["v"], **kw)
-    for _ in range(warmup):
-        fn(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)
-    stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(steps):
-        fn(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps  # ms per step (= per launch)
+    launch = lambda: fn(dev["q"], dev["k"], dev["v"], out=o, lse=lse, **kw)
+    n_warm = warm_up(launch, warmup)
+    ms, per = timed(launch, steps, torch.cuda.current_stream())
+    if stats is not None:
+        srt = sorted(per)
+        stats.update(warmup_launches=n_warm,
+                     launch_ms={"first": round(per[0], 5), "last": round(per[-1], 5),
+                                "min": round(srt[0], 5), "median": round(srt[len(srt) // 2], 5),
+                                "max": round(srt[-1], 5)})
+    return ms  # ms per step (= per launch)
 
 
 def time_backward(inp, dev, steps, warmup):
@@ -189,17 +228,10 @@ def time_backward(inp, dev, steps, warmup):
     dq, dk, dv = bwd(dev["q"], dev["k"], dev["v"], o, do, lse, **kw)
     ws = torch.empty(fa.fa_bwd_workspace_size(inp["B"] * inp["Nq"], inp["Hq"], inp["d"]),
                      dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
-        bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
-    stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(steps):
-        bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    launch = lambda: bwd(dev["q"], dev["k"], dev["v"], o, do, lse, dq=dq, dk=dk, dv=dv,
+                         workspace=ws, **kw)
+    warm_up(launch, warmup)
+    return timed(launch, steps, torch.cuda.current_stream())[0]
 
 
 def decode_pairs(inp):
@@ -239,17 +271,9 @@ def time_decode(inp, steps, warmup):
     lse = torch.empty((B, hq, nq), dtype=torch.float32, device="cuda")
     kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"], seqlens_k=lens,
               num_splits=splits, out=o, lse=lse, workspace=ws)
-    for _ in range(warmup + 1):
-        fa.fa_decode(q, k, v, **kw)
-    stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(steps):
-        fa.fa_decode(q, k, v, **kw)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps, splits
+    launch = lambda: fa.fa_decode(q, k, v, **kw)
+    warm_up(launch, warmup + 1)
+    return timed(launch, steps, torch.cuda.current_stream())[0], splits
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -298,7 +322,8 @@ def main(argv=None):
 
     inp = workloads.make_inputs(a.workload)
     dev = device_inputs(inp)
-    ms = time_forward(inp, dev, a.steps, a.warmup)
+    stats = {}
+    ms = time_forward(inp, dev, a.steps, a.warmup, stats)
     flops = attention_flops(inp)
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = traffic_from_profile(a.workload)
@@ -320,6 +345,9 @@ def main(argv=None):
         "dtype": inp["dtype"],
         "data": "synthetic",
         "config": cfg,
+        "warmup_launches": stats["warmup_launches"],
+        "min_warmup_ms": MIN_WARMUP_MS,
+        "launch_ms": stats["launch_ms"],
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(algorithmic_bytes(inp) / (ms * 1e-3) / 1e9, 1),
         "roofline": {

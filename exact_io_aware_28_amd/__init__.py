@@ -99,59 +99,141 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _launch_stream(stream):
+    """The torch stream the call runs on (the current one by default)."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
 
 
-def _geometry(q, k, cu_seqlens, max_seqlen):
-    """(B, Hq, Hkv, Nq, Nk, d) from the tensor shapes (layouts of the ABI)."""
+def _on(stream):
+    """Context for the binding's own allocations: made on the stream that the
+    kernels read and write them on, so that the caching allocator never hands
+    their memory to other work while those kernels may still use it."""
+    import torch
+    return torch.cuda.stream(stream)
+
+
+# ------------------------------------------------------------------ checks
+# Every wrapper checks all of its arguments before anything is allocated or
+# launched: first what the host can see (types, dtypes, shapes, contiguity,
+# sizes), then that every tensor lives on q's device.  A pointer the kernels
+# would misread (a host address, int64 offsets, a short output) is refused
+# here rather than faulting on the GPU.
+
+def _tensor(name, t, dtype, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _optional(name, t, dtype, shape):
+    return None if t is None else _tensor(name, t, dtype, shape)
+
+
+def _workspace(t, nbytes):
+    """A caller-supplied scratch buffer: any dtype, contiguous, at least
+    `nbytes` long."""
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"workspace holds {_nbytes(t)} bytes, needs {nbytes}")
+    return t
+
+
+def _same_device(device, named):
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _geometry(q, k, v, cu_seqlens, max_seqlen, dtype):
+    """Check q, k, v (and cu_seqlens) against each other and the layouts of
+    the C ABI (host-visible facts only); returns (B, Hq, Hkv, Nq, Nk, d)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _tensor(name, t, dtype)
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError(f"k and v must have the same shape, got {tuple(k.shape)} "
+                         f"and {tuple(v.shape)}")
     if cu_seqlens is None:
         if q.dim() != 4 or k.dim() != 4:
             raise ValueError("dense q/k/v must be [B, N, H, d]")
         B, nq, hq, d = q.shape
-        nk, hkv = k.shape[1], k.shape[2]
-        return B, hq, hkv, nq, nk, d
+        if k.shape[0] != B:
+            raise ValueError(f"k has batch {k.shape[0]}, q has {B}")
+        if k.shape[3] != d:
+            raise ValueError(f"k has head dimension {k.shape[3]}, q has {d}")
+        return B, hq, k.shape[2], nq, k.shape[1], d
     if q.dim() != 3 or k.dim() != 3:
         raise ValueError("packed q/k/v must be [T, H, d]")
-    if max_seqlen is None:
-        raise ValueError("packed batches need max_seqlen")
+    if k.shape[0] != q.shape[0]:
+        raise ValueError(f"packed k has {k.shape[0]} tokens, q has {q.shape[0]}")
+    if k.shape[2] != q.shape[2]:
+        raise ValueError(f"k has head dimension {k.shape[2]}, q has {q.shape[2]}")
+    _tensor("cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with B + 1 >= 2 offsets")
+    if max_seqlen is None or int(max_seqlen) < 1:
+        raise ValueError("packed batches need max_seqlen >= 1")
     B = cu_seqlens.numel() - 1
     return B, q.shape[1], k.shape[1], int(max_seqlen), int(max_seqlen), q.shape[2]
-
-
-def _check(tensors, dtype):
-    for name, t in tensors.items():
-        if t.dtype != dtype:
-            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
 
 
 def _lse_shape(q, B, hq, nq, cu_seqlens):
     return (B, hq, nq) if cu_seqlens is None else (hq, q.shape[0])
 
 
-def _fwd(fn, dtype, q, k, v, scale, causal, window, cu_seqlens, max_seqlen, out,
-         lse, stream):
+def _alloc(t, shape, dtype, stream, device):
+    """t if the caller supplied it, else a new tensor made on `stream`."""
     import torch
-    _check({"q": q, "k": k, "v": v}, dtype)
-    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
+    if t is not None:
+        return t
+    with _on(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _stream_arg(s):
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ forward
+def _fwd(fn, dtype, q, k, v, scale, causal, window, cu_seqlens, max_seqlen, out, lse,
+         stream, extra=()):
+    import torch
+    B, hq, hkv, nq, nk, d = _geometry(q, k, v, cu_seqlens, max_seqlen, dtype)
+    lse_shape = _lse_shape(q, B, hq, nq, cu_seqlens)
+    _optional("out", out, dtype, q.shape)
+    _optional("lse", lse, torch.float32, lse_shape)
+    _same_device(q.device, [("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens),
+                            ("out", out), ("lse", lse)])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty(_lse_shape(q, B, hq, nq, cu_seqlens), dtype=torch.float32,
-                          device=q.device)
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
+    s = _launch_stream(stream)
+    out = _alloc(out, q.shape, dtype, s, q.device)
+    lse = _alloc(lse, lse_shape, torch.float32, s, q.device)
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv, nq, nk, d,
-            float(scale), int(bool(causal)), int(window), _ptr(cu_seqlens),
-            _stream(stream))
+            float(scale), int(bool(causal)), int(window), _ptr(cu_seqlens), *extra,
+            _stream_arg(s))
     if st != FA_OK:
         raise FaError(st, fn.__name__)
     return out, lse
@@ -181,54 +263,63 @@ def fa_fwd_f32(q, k, v, scale=None, causal=False, window=0, cu_seqlens=None,
                 cu_seqlens, max_seqlen, out, lse, stream)
 
 
-def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
-           cu_seqlens=None, max_seqlen=None, dq=None, dk=None, dv=None,
-           workspace=None, stream=None):
-    """bf16 backward by recomputation; returns (dq, dk, dv)."""
-    import torch
-    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, torch.bfloat16)
-    _check({"lse": lse}, torch.float32)
-    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                      workspace.numel() * workspace.element_size(),
-                      B, hq, hkv, nq, nk, d, float(scale), int(bool(causal)),
-                      int(window), _ptr(cu_seqlens), _stream(stream))
-    if st != FA_OK:
-        raise FaError(st, "fa_bwd")
-    return dq, dk, dv
-
-
 def fa_fwd_dropout(q, k, v, dropout_p, seed, scale=None, causal=False, window=0,
                    cu_seqlens=None, max_seqlen=None, out=None, lse=None, stream=None):
     """bf16 forward with dropout on the probabilities (Philox keep-mask of
     the public header); returns (o bf16, lse fp32 of the undropped P).
     dropout_p is passed as a C float."""
     import torch
-    _check({"q": q, "k": k, "v": v}, torch.bfloat16)
-    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
+    return _fwd(lib().fa_fwd_dropout, torch.bfloat16, q, k, v, scale, causal, window,
+                cu_seqlens, max_seqlen, out, lse, stream,
+                extra=(float(dropout_p), int(seed)))
+
+
+# ------------------------------------------------------------------ backward
+def _bwd_prepare(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, dq, dk, dv, workspace,
+                 stream, bias=None):
+    """Checks and outputs shared by the backward wrappers."""
+    import torch
+    B, hq, hkv, nq, nk, d = _geometry(q, k, v, cu_seqlens, max_seqlen, torch.bfloat16)
+    _tensor("o", o, torch.bfloat16, q.shape)
+    _tensor("dout", dout, torch.bfloat16, q.shape)
+    _tensor("lse", lse, torch.float32, _lse_shape(q, B, hq, nq, cu_seqlens))
+    _optional("dq", dq, torch.bfloat16, q.shape)
+    _optional("dk", dk, torch.bfloat16, k.shape)
+    _optional("dv", dv, torch.bfloat16, v.shape)
+    ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
+    _workspace(workspace, ws_bytes)
+    bview = None if bias is None else _bias_view(bias, B, hq, nq, nk)
+    _same_device(q.device, [("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout),
+                            ("lse", lse), ("cu_seqlens", cu_seqlens), ("dq", dq), ("dk", dk),
+                            ("dv", dv), ("workspace", workspace),
+                            ("bias", None if bias is None else bias)])
+    s = _launch_stream(stream)
+    dq = _alloc(dq, q.shape, torch.bfloat16, s, q.device)
+    dk = _alloc(dk, k.shape, torch.bfloat16, s, q.device)
+    dv = _alloc(dv, v.shape, torch.bfloat16, s, q.device)
+    ws = _alloc(workspace, (max(ws_bytes, 1),), torch.uint8, s, q.device)
+    return (B, hq, hkv, nq, nk, d), s, dq, dk, dv, ws, bview
+
+
+def _bwd_call(name, args, geo, scale, causal, window, tail, s):
+    B, hq, hkv, nq, nk, d = geo
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty(_lse_shape(q, B, hq, nq, cu_seqlens), dtype=torch.float32,
-                          device=q.device)
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
-    st = lib().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv,
-                              nq, nk, d, float(scale), int(bool(causal)), int(window),
-                              _ptr(cu_seqlens), float(dropout_p), int(seed), _stream(stream))
+    st = getattr(lib(), name)(*args, B, hq, hkv, nq, nk, d, float(scale), int(bool(causal)),
+                              int(window), *tail, _stream_arg(s))
     if st != FA_OK:
-        raise FaError(st, "fa_fwd_dropout")
-    return out, lse
+        raise FaError(st, name)
+
+
+def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
+           cu_seqlens=None, max_seqlen=None, dq=None, dk=None, dv=None,
+           workspace=None, stream=None):
+    """bf16 backward by recomputation; returns (dq, dk, dv)."""
+    geo, s, dq, dk, dv, ws, _ = _bwd_prepare(q, k, v, o, dout, lse, cu_seqlens, max_seqlen,
+                                             dq, dk, dv, workspace, stream)
+    args = [_ptr(x) for x in (q, k, v, o, dout, lse, dq, dk, dv, ws)] + [_nbytes(ws)]
+    _bwd_call("fa_bwd", args, geo, scale, causal, window, [_ptr(cu_seqlens)], s)
+    return dq, dk, dv
 
 
 def fa_bwd_dropout(q, k, v, o, dout, lse, dropout_p, seed, scale=None, causal=False,
@@ -236,43 +327,38 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, dropout_p, seed, scale=None, causal=Fa
                    workspace=None, stream=None):
     """bf16 backward of fa_fwd_dropout (same dropout_p and seed); returns
     (dq, dk, dv)."""
-    import torch
-    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, torch.bfloat16)
-    _check({"lse": lse}, torch.float32)
-    B, hq, hkv, nq, nk, d = _geometry(q, k, cu_seqlens, max_seqlen)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    st = lib().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(),
-                              B, hq, hkv, nq, nk, d, float(scale), int(bool(causal)),
-                              int(window), _ptr(cu_seqlens), float(dropout_p), int(seed),
-                              _stream(stream))
-    if st != FA_OK:
-        raise FaError(st, "fa_bwd_dropout")
+    geo, s, dq, dk, dv, ws, _ = _bwd_prepare(q, k, v, o, dout, lse, cu_seqlens, max_seqlen,
+                                             dq, dk, dv, workspace, stream)
+    args = [_ptr(x) for x in (q, k, v, o, dout, lse, dq, dk, dv, ws)] + [_nbytes(ws)]
+    _bwd_call("fa_bwd_dropout", args, geo, scale, causal, window,
+              [_ptr(cu_seqlens), float(dropout_p), int(seed)], s)
     return dq, dk, dv
 
 
+# ------------------------------------------------------------------ bias
 def _bias_view(bias, B, hq, nq, nk):
-    """(tensor, stride_b, stride_h, stride_q): an fp32 device bias that
-    broadcasts to [B, Hq, Nq, Nk] as a strided view (no copy unless its key
-    dimension is not contiguous)."""
+    """(tensor, stride_b, stride_h, stride_q): an fp32 bias that broadcasts
+    to [B, Hq, Nq, Nk] as a strided view (no copy unless its key dimension is
+    not contiguous)."""
     import torch
-    if bias.dtype != torch.float32 or not bias.is_cuda:
-        raise TypeError("bias must be a float32 device tensor")
+    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32:
+        raise TypeError("bias must be a float32 tensor")
     if bias.dim() > 4:
         raise ValueError("bias must broadcast to [B, Hq, Nq, Nk]")
-    if bias.stride(-1) != 1 and bias.shape[-1] != 1:
-        bias = bias.contiguous()
     if bias.shape[-1] == 1 and nk != 1:
         raise ValueError("the key dimension of the bias cannot broadcast")
     b4 = bias.reshape((1,) * (4 - bias.dim()) + tuple(bias.shape)) if bias.dim() < 4 else bias
+    try:
+        b4.expand(B, hq, nq, nk)
+    except RuntimeError as exc:
+        raise ValueError(f"bias of shape {tuple(bias.shape)} does not broadcast to "
+                         f"{(B, hq, nq, nk)}") from exc
+    return b4
+
+
+def _bias_strides(b4, B, hq, nq, nk):
+    if b4.stride(-1) != 1 and nk != 1:  # the kernels read keys at unit stride
+        b4 = b4.contiguous()
     e = b4.expand(B, hq, nq, nk)
     return e, e.stride(0), e.stride(1), e.stride(2)
 
@@ -282,17 +368,21 @@ def fa_fwd_bias(q, k, v, bias, scale=None, causal=False, window=0, out=None, lse
     """bf16 forward with an additive fp32 bias that broadcasts to
     [B, Hq, Nq, Nk]; returns (o bf16, lse fp32).  Dense batches only."""
     import torch
-    _check({"q": q, "k": k, "v": v}, torch.bfloat16)
-    B, hq, hkv, nq, nk, d = _geometry(q, k, None, None)
+    B, hq, hkv, nq, nk, d = _geometry(q, k, v, None, None, torch.bfloat16)
+    b4 = _bias_view(bias, B, hq, nq, nk)
+    _optional("out", out, torch.bfloat16, q.shape)
+    _optional("lse", lse, torch.float32, (B, hq, nq))
+    _same_device(q.device, [("q", q), ("k", k), ("v", v), ("bias", bias), ("out", out),
+                            ("lse", lse)])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
-    bt, sb, sh, sq = _bias_view(bias, B, hq, nq, nk)
+    s = _launch_stream(stream)
+    bt, sb, sh, sq = _bias_strides(b4, B, hq, nq, nk)
+    out = _alloc(out, q.shape, torch.bfloat16, s, q.device)
+    lse = _alloc(lse, (B, hq, nq), torch.float32, s, q.device)
     st = lib().fa_fwd_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv, nq,
                            nk, d, float(scale), int(bool(causal)), int(window), _ptr(bt),
-                           sb, sh, sq, _stream(stream))
+                           sb, sh, sq, _stream_arg(s))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_bias")
     return out, lse
@@ -302,29 +392,16 @@ def fa_bwd_bias(q, k, v, bias, o, dout, lse, scale=None, causal=False, window=0,
                 dq=None, dk=None, dv=None, workspace=None, stream=None):
     """bf16 backward of fa_fwd_bias (the bias is a constant); returns
     (dq, dk, dv)."""
-    import torch
-    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout}, torch.bfloat16)
-    _check({"lse": lse}, torch.float32)
-    B, hq, hkv, nq, nk, d = _geometry(q, k, None, None)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    bt, sb, sh, sq = _bias_view(bias, B, hq, nq, nk)
-    st = lib().fa_bwd_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(),
-                           B, hq, hkv, nq, nk, d, float(scale), int(bool(causal)),
-                           int(window), _ptr(bt), sb, sh, sq, _stream(stream))
-    if st != FA_OK:
-        raise FaError(st, "fa_bwd_bias")
+    geo, s, dq, dk, dv, ws, b4 = _bwd_prepare(q, k, v, o, dout, lse, None, None, dq, dk, dv,
+                                              workspace, stream, bias=bias)
+    B, hq, hkv, nq, nk, d = geo
+    bt, sb, sh, sq = _bias_strides(b4, B, hq, nq, nk)
+    args = [_ptr(x) for x in (q, k, v, o, dout, lse, dq, dk, dv, ws)] + [_nbytes(ws)]
+    _bwd_call("fa_bwd_bias", args, geo, scale, causal, window, [_ptr(bt), sb, sh, sq], s)
     return dq, dk, dv
 
 
+# ------------------------------------------------------------------ decode
 def fa_decode_workspace_size(B, Hq, Nq, d, num_splits):
     return int(lib().fa_decode_workspace_size(int(B), int(Hq), int(Nq), int(d),
                                               int(num_splits)))
@@ -334,29 +411,42 @@ def fa_decode_num_splits(B, Hq, Hkv, Nq, Nk):
     return int(lib().fa_decode_num_splits(int(B), int(Hq), int(Hkv), int(Nq), int(Nk)))
 
 
+def _decode_prepare(q, k, v, seqlens_k, num_splits, out, lse, workspace, stream,
+                    need_workspace=True):
+    import torch
+    B, hq, hkv, nq, nk, d = _geometry(q, k, v, None, None, torch.bfloat16)
+    if seqlens_k is not None:
+        _tensor("seqlens_k", seqlens_k, torch.int32, (B,))
+    if num_splits is None:
+        num_splits = fa_decode_num_splits(B, hq, hkv, nq, nk)
+    num_splits = int(num_splits)
+    _optional("out", out, torch.bfloat16, q.shape)
+    _optional("lse", lse, torch.float32, (B, hq, nq))
+    ws_bytes = fa_decode_workspace_size(B, hq, nq, d, num_splits) if need_workspace else 0
+    if need_workspace:
+        _workspace(workspace, ws_bytes)
+    _same_device(q.device, [("q", q), ("k", k), ("v", v), ("seqlens_k", seqlens_k),
+                            ("out", out), ("lse", lse), ("workspace", workspace)])
+    s = _launch_stream(stream)
+    out = _alloc(out, q.shape, torch.bfloat16, s, q.device)
+    lse = _alloc(lse, (B, hq, nq), torch.float32, s, q.device)
+    ws = _alloc(workspace, (max(ws_bytes, 1),), torch.uint8, s, q.device) \
+        if need_workspace else None
+    return (B, hq, hkv, nq, nk, d), num_splits, s, out, lse, ws
+
+
 def fa_decode(q, k, v, scale=None, causal=False, window=0, seqlens_k=None,
               num_splits=None, out=None, lse=None, workspace=None, stream=None):
     """Split-KV attention of a few query rows per sequence over a K/V cache;
     returns (o bf16 [B, Nq, Hq, d], lse fp32 [B, Hq, Nq])."""
-    import torch
-    _check({"q": q, "k": k, "v": v}, torch.bfloat16)
-    B, hq, hkv, nq, nk, d = _geometry(q, k, None, None)
+    (B, hq, hkv, nq, nk, d), num_splits, s, out, lse, ws = _decode_prepare(
+        q, k, v, seqlens_k, num_splits, out, lse, workspace, stream)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if seqlens_k is not None and seqlens_k.dtype != torch.int32:
-        raise TypeError("seqlens_k must be int32")
-    if num_splits is None:
-        num_splits = fa_decode_num_splits(B, hq, hkv, nq, nk)
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device)
-    ws_bytes = fa_decode_workspace_size(B, hq, nq, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     st = lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv, nq,
                          nk, d, float(scale), int(bool(causal)), int(window),
-                         _ptr(seqlens_k), int(num_splits), _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), _stream(stream))
+                         _ptr(seqlens_k), num_splits, _ptr(ws), _nbytes(ws), _stream_arg(s))
     if st != FA_OK:
         raise FaError(st, "fa_decode")
     return out, lse
+

@@ -61,12 +61,23 @@ def o_errors(o, ref):
     return float(err.max()), float(err.mean())
 
 
-def check_o(o, ref, what=""):
+def check_o(o, ref, what="", bar_scale=1.0):
+    """O against the bars; bar_scale > 1 only where a derived bar applies
+    (dropout above p = 0.5, whose kept values grow by 1 / (1 - p))."""
     mx, mn = o_errors(o, ref)
-    say(f"  {what} O max|err|={mx:.3e} mean|err|={mn:.3e}")
+    say(f"  {what} O max|err|={mx:.3e} mean|err|={mn:.3e}"
+        + (f" (bars x{bar_scale:.3g})" if bar_scale != 1.0 else ""))
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
-    assert mx <= O_MAX and mn <= O_MEAN, (what, mx, mn)
+    assert mx <= O_MAX * bar_scale and mn <= O_MEAN * bar_scale, (what, mx, mn)
     return mx, mn
+
+
+def dropout_bar_scale(p):
+    """Bar multiplier for O with dropout probability p: 1 (the stated bars)
+    for p <= 0.5.  Above that the kept probabilities, O itself and its bf16
+    rounding all grow by 1 / (1 - p) (10x at p = 0.9) while the inputs do
+    not, so the bars grow by the same factor."""
+    return 1.0 if p <= 0.5 else 1.0 / (1.0 - p)
 
 
 def check_lse(lse, ref, what=""):
@@ -109,4 +120,5 @@ def is_close_bits(a, b):
 
 
 __all__ = ["say", "to_dev", "to_np", "run_fwd", "run_bwd", "check_o", "check_lse",
+           "dropout_bar_scale",
            "check_grad", "sample_rows", "math"]

@@ -31,7 +31,9 @@ def _dense(rng, B, nq, nk, hq, hkv, d):
 
 # ---------------------------------------------------------------- P-1
 def check_rows_sum_to_one(A):
-    """Every row of P with a visible key sums to 1 (softmax definition)."""
+    """Every row of P with a visible key sums to 1 (softmax definition), and
+    P equals torch's float64 softmax of the scaled scores with the causal
+    (bottom-right) and window entries filled with -inf."""
     rng = _rng(11)
     q = rng.standard_normal((37, 16))
     k = rng.standard_normal((53, 16))
@@ -39,6 +41,16 @@ def check_rows_sum_to_one(A):
         p = A.probabilities(q, k, 0.7, causal, window)
         assert np.all(p >= 0)
         assert np.allclose(p.sum(axis=1), 1.0, atol=1e-12)
+        s = 0.7 * torch.from_numpy(q) @ torch.from_numpy(k).T
+        i = torch.arange(37)[:, None] + (53 - 37)
+        j = torch.arange(53)[None, :]
+        hide = torch.zeros(37, 53, dtype=torch.bool)
+        if causal:
+            hide |= j > i
+        if window > 0:
+            hide |= (i - j) >= window
+        ref = torch.softmax(s.masked_fill(hide, float("-inf")), dim=1).numpy()
+        assert np.allclose(p, ref, atol=1e-13, rtol=0)
 
 
 # ---------------------------------------------------------------- P-2
@@ -518,6 +530,58 @@ def check_dropout_mask_statistics(A):
     assert philox.keep_mask(7, 0, 0, np.arange(8), 64, 0.0).all()
 
 
+def load_dropout_golden():
+    """Rows of tests/golden/dropout_keep_slots.txt as dicts: the element
+    (seed, b, h, i, j), the Philox counter and key written out by hand from
+    the mask's definition, the output word and half holding its slot, and
+    (zero-counter rows only) the published 16-bit slot value with its keep
+    bits at p = 0.5 and p = 0.75."""
+    rows = []
+    with open(os.path.join(GOLDEN, "dropout_keep_slots.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            elem, ctr, slot, val = (x.split() for x in line.split("|"))
+            seed = int(elem[0], 16)
+            b, h, i, j = (int(x) for x in elem[1:])
+            c = [int(x) for x in ctr[:4]] + [int(x, 16) for x in ctr[4:]]
+            u16 = None if val[0] == "-" else int(val[0], 16)
+            keeps = None if u16 is None else {0.5: val[1] == "1", 0.75: val[2] == "1"}
+            rows.append(dict(seed=seed, b=b, h=h, i=i, j=j, counter=c[:4], key=c[4:],
+                             word=int(slot[0]), half=int(slot[1]), u16=u16, keeps=keeps))
+    return rows
+
+
+def golden_slot_value(row):
+    """The 16-bit slot of a golden row: the published value, else the
+    generator (pinned by its known-answer vectors) at the row's hand-written
+    counter and key."""
+    from oracle import philox
+    if row["u16"] is not None:
+        return row["u16"]
+    words = philox.philox4x32_10(*row["counter"], *row["key"])
+    return (int(words[row["word"]]) >> (16 * row["half"])) & 0xFFFF
+
+
+def check_dropout_slots_golden(A):
+    """The oracle's keep-mask takes each element's decision from the call and
+    slot that the hand-worked table assigns it (key -> counter word, output
+    word and half; row, head and sequence -> the other counter words; seed ->
+    key), at several p; on the zero counter the slots and keep bits are the
+    published generator output itself."""
+    rows = load_dropout_golden()
+    assert len(rows) == 20
+    for r in rows:
+        u = golden_slot_value(r)
+        assert r["seed"] & 0xFFFFFFFF == r["key"][0] and r["seed"] >> 32 == r["key"][1]
+        for p in (0.1, 0.5, 0.75, 0.9):
+            keep = A._keep(p, r["seed"], r["b"], r["h"], np.array([r["i"]]), r["j"] + 1)
+            want = u >= int(p * 65536)
+            assert bool(keep[0, r["j"]]) == want, (r, p, hex(u))
+            if r["keeps"] is not None and p in r["keeps"]:
+                assert want == r["keeps"][p], (r, p)
+
+
 def _torch_dropout_reference(q, k, v, scale, causal, keep, p):
     """O = (softmax(S) * Z / (1 - p)) V in float64 torch, one head [n, d]."""
     tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
@@ -613,7 +677,8 @@ ALL_FORWARD = [check_rows_sum_to_one, check_identical_keys, check_dominant_score
                check_empty_rows, check_bias_against_torch_sdpa,
                check_bias_row_constant, check_bias_is_key_shift,
                check_bias_mask_equals_causal, check_philox_known_answers,
-               check_dropout_mask_statistics, check_dropout_matches_masked_softmax,
+               check_dropout_mask_statistics, check_dropout_slots_golden,
+               check_dropout_matches_masked_softmax,
                check_dropout_unbiased]
 ALL_BACKWARD = [check_backward_finite_differences, check_backward_autograd,
                 check_backward_invariants, check_bias_backward_autograd,

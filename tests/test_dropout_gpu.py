@@ -23,7 +23,9 @@ import pytest
 import oracle
 import workloads
 from oracle import philox
-from tests.gpu_util import check_grad, check_lse, check_o, say, sample_rows, to_dev, to_np
+from tests.gpu_util import (check_grad, check_lse, check_o, dropout_bar_scale, say, sample_rows,
+                            to_dev, to_np)
+from tests.oracle_pins import golden_slot_value, load_dropout_golden
 
 pytestmark = pytest.mark.gpu
 
@@ -167,6 +169,45 @@ def test_dropout_mask_bit_exact(case):
         f"{float((o != 0).sum()) / max(checked, 1):.3f} (expected {1 - pf:.3f})")
 
 
+GOLDEN_ROWS = load_dropout_golden()
+
+
+@pytest.mark.parametrize("row", range(len(GOLDEN_ROWS)), ids=lambda r: f"g{r}")
+def test_dropout_golden_slots(row):
+    """Each element of the hand-worked table tests/golden/dropout_keep_slots.txt,
+    probed alone in the forward, the dK/dV and the dQ kernels: Q = 0 and K, V
+    zero except K[j] = e_1, V[j] = e_0 (so every visible probability of row i
+    is 1 / N), dO zero except dO[i] = e_0.  Then O[i, 0], dV[j, 0] and
+    dQ[i, 1] = (1/N) (s - s/N) (s the keep scale) are non-zero iff element
+    (i, j) is kept."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    r = GOLDEN_ROWS[row]
+    seed, b, h, i, j = r["seed"], r["b"], r["h"], r["i"], r["j"]
+    # N >= 2: with one key P = 1 and dS = P (dP - D) vanishes whatever the mask
+    B, H, N, d = b + 1, h + 1, max(i, j) + 2, 64
+    u = golden_slot_value(r)
+    say(f"[dropout golden] row {row}: seed={seed:#x} b={b} h={h} i={i} j={j} slot={u:#06x} "
+        f"B={B} H={H} N={N}")
+    z = lambda: torch.zeros((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    q, k, v, do = z(), z(), z(), z()
+    k[b, j, h, 1] = 1.0
+    v[b, j, h, 0] = 1.0
+    do[b, i, h, 0] = 1.0
+    for p in (0.1, 0.5, 0.75):
+        pf = _f32(p)
+        want = u >= int(pf * 65536)
+        if r["keeps"] is not None and p in r["keeps"]:
+            assert want == r["keeps"][p]
+        o, lse = fa.fa_fwd_dropout(q, k, v, pf, seed, scale=1.0)
+        dq, dk, dv = fa.fa_bwd_dropout(q, k, v, o, do, lse, pf, seed, scale=1.0)
+        torch.cuda.synchronize()
+        got = (float(o[b, i, h, 0]) != 0.0, float(dv[b, j, h, 0]) != 0.0,
+               float(dq[b, i, h, 1]) != 0.0)
+        assert got == (want, want, want), (row, p, got, want)
+        assert int(torch.count_nonzero(dk)) == 0  # Q = 0: no dK anywhere
+
+
 # ------------------------------------------------------------ attention parity
 CASES = [
     # B, Nq, Nk, Hq, Hkv, d, causal, window, p, seed
@@ -191,10 +232,7 @@ def test_dropout_dense(case):
     f = lambda n: inp[n].astype(np.float64)
     o_ref, lse_ref = oracle.attn_fwd(f("q"), f("k"), f("v"), inp["scale"], causal, window,
                                      dropout_p=pf, seed=seed)
-    # kept probabilities are scaled by 1 / (1 - p), and so is O and its bf16
-    # rounding error: compare (1 - p) O, which has the magnitude of
-    # attention without dropout, against the bars
-    check_o((1.0 - pf) * to_np(o), (1.0 - pf) * o_ref, what)
+    check_o(to_np(o), o_ref, what, dropout_bar_scale(pf))
     check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, what)
     ref = oracle.attn_bwd(f("q"), f("k"), f("v"), f("do"), inp["scale"], causal, window,
                           dropout_p=pf, seed=seed)
@@ -212,7 +250,7 @@ def test_dropout_packed():
     cu = inp["cu_seqlens"]
     o_ref, lse_ref = oracle.attn_fwd(f("q"), f("k"), f("v"), inp["scale"], True, 100, cu,
                                      dropout_p=pf, seed=seed)
-    check_o((1.0 - pf) * to_np(o), (1.0 - pf) * o_ref, "packed")
+    check_o(to_np(o), o_ref, "packed", dropout_bar_scale(pf))
     check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, "packed")
     ref = oracle.attn_bwd(f("q"), f("k"), f("v"), f("do"), inp["scale"], True, 100, cu,
                           dropout_p=pf, seed=seed)
@@ -258,8 +296,8 @@ def test_dropout_gqa_prefill_sampled():
         outs.append(o[0, rows, h])
         refs.append(ro)
         lerr = max(lerr, float(np.abs(lse[0, h, rows] - rl).max()))
-    check_o((1.0 - pf) * np.concatenate(outs), (1.0 - pf) * np.concatenate(refs),
-            "gqa prefill dropout fwd")
+    check_o(np.concatenate(outs), np.concatenate(refs), "gqa prefill dropout fwd",
+            dropout_bar_scale(pf))
     say(f"  LSE max|err|={lerr:.3e}")
     assert lerr <= 1e-3
     dq, dk, dv = to_np(dq), to_np(dk), to_np(dv)

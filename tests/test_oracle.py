@@ -27,6 +27,8 @@ def _mutant(**overrides):
     m = types.ModuleType("oracle_mutant")
     m.__dict__.update({k: v for k, v in A.__dict__.items()
                        if not k.startswith("__")})
+    # the copied functions look builtins up through their globals
+    m.__dict__["__builtins__"] = A.__dict__["__builtins__"]
     # functions look up globals in their defining module: rebind them
     for name, obj in list(m.__dict__.items()):
         if isinstance(obj, types.FunctionType) and obj.__module__ == A.__name__:
@@ -153,6 +155,46 @@ def _keep_rows_keys_swapped(dropout_p, seed, b, h, rows, nk):
     return u16 >= np.uint64(philox.drop_threshold(dropout_p))
 
 
+def _keep_slots_from_low_bits(dropout_p, seed, b, h, rows, nk):
+    """A plausible mapping mistake: eight consecutive keys share a call
+    (counter word j >> 3) and take slot j & 7."""
+    if dropout_p == 0.0:
+        return None
+    from oracle import philox
+    rows = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(nk)[None, :]
+    slot = j & 7
+    w = philox.philox4x32_10(j >> 3, rows, h, b, seed & 0xFFFFFFFF, seed >> 32)
+    word = slot >> 1
+    u = np.select([word == 0, word == 1, word == 2, word == 3], w)
+    u16 = (u >> (np.uint64(16) * (slot & 1).astype(np.uint64))) & np.uint64(0xFFFF)
+    return u16 >= np.uint64(philox.drop_threshold(dropout_p))
+
+
+def _keep_head_and_batch_swapped(dropout_p, seed, b, h, rows, nk):
+    return A._keep(dropout_p, seed, h, b, rows, nk)
+
+
+def _keep_halves_swapped(dropout_p, seed, b, h, rows, nk):
+    """Slot s read from the other 16-bit half of its word."""
+    if dropout_p == 0.0:
+        return None
+    from oracle import philox
+    rows = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(nk)[None, :]
+    c0 = 2 * (j >> 4) + ((j >> 2) & 1)
+    slot = 4 * ((j >> 3) & 1) + (j & 3)
+    w = philox.philox4x32_10(c0, rows, h, b, seed & 0xFFFFFFFF, seed >> 32)
+    word = slot >> 1
+    u = np.select([word == 0, word == 1, word == 2, word == 3], w)
+    u16 = (u >> (np.uint64(16) * (1 - (slot & 1)).astype(np.uint64))) & np.uint64(0xFFFF)
+    return u16 >= np.uint64(philox.drop_threshold(dropout_p))
+
+
+def _probabilities_unscaled(q, k, scale, causal=False, window=0):
+    return A.probabilities(q, k, 1.0, causal, window)
+
+
 def _head_bwd_dropout_dp_unmasked(q, k, v, do, scale, ok, bias=None, keep=None, p_drop=0.0):
     o, _, p = A._head_fwd(q, k, v, scale, ok, bias, keep, p_drop)
     dv = A._dropped(p, keep, p_drop).T @ do
@@ -179,6 +221,10 @@ MUTATIONS = {
     "dropout_unscaled": dict(_dropped=_dropped_unscaled),
     "dropout_rows_keys_swapped": dict(_keep=_keep_rows_keys_swapped),
     "dropout_dp_unmasked": dict(_head_bwd=_head_bwd_dropout_dp_unmasked),
+    "dropout_slots_from_low_bits": dict(_keep=_keep_slots_from_low_bits),
+    "dropout_head_batch_swapped": dict(_keep=_keep_head_and_batch_swapped),
+    "dropout_slot_halves_swapped": dict(_keep=_keep_halves_swapped),
+    "probabilities_unscaled": dict(probabilities=_probabilities_unscaled),
 }
 
 
@@ -186,6 +232,30 @@ MUTATIONS = {
 def test_pins_catch_planted_mistake(name):
     mutant = _mutant(**MUTATIONS[name])
     assert _caught(mutant, pins.ALL_FORWARD + pins.ALL_BACKWARD), name
+
+
+def _slot_words_low_bits(j):
+    j = np.asarray(j, dtype=np.int64)
+    return j >> 3, (j & 7) >> 1, j & 1
+
+
+def _slot_words_no_call_pairing(j):
+    j = np.asarray(j, dtype=np.int64)
+    return j >> 3, (j & 7) >> 1 & 3, (j & 7) & 1
+
+
+@pytest.mark.parametrize("wrong", [_slot_words_low_bits, _slot_words_no_call_pairing])
+def test_golden_slots_catch_a_mapping_mistake_in_the_generator_module(monkeypatch, wrong):
+    """A key -> slot mistake inside oracle/philox.py reaches every user of the
+    keep-mask at once, so pins that compare the oracle with itself cannot see
+    it; the hand-worked golden table must."""
+    from oracle import philox
+    monkeypatch.setattr(philox, "slot_words", wrong)
+    with pytest.raises(AssertionError):
+        pins.check_dropout_slots_golden(A)
+    # the self-consistency pin passes on the same mistake: it is not a pin
+    # of the mapping
+    pins.check_dropout_matches_masked_softmax(A)
 
 
 def test_mutant_harness_is_faithful():
