@@ -16,6 +16,8 @@ Functions mirror the C ABI in include/fa_mi355x.h:
     fa_decode(q, k, v, scale, causal, window, seqlens_k, num_splits) -> (o, lse)
     fa_decode_workspace_size(B, Hq, Nq, d, num_splits) -> int
     fa_decode_num_splits(B, Hq, Hkv, Nq, Nk) -> int
+    fa_decode_noalloc(q, k, v, out, lse, ...) -> (out, lse), no allocation
+    fa_decode_noalloc_max_splits(B, Hq, Nq, d) -> int
     fa_status_string(status) -> str
 """
 
@@ -26,7 +28,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+# bytes of the static device array behind fa_decode_noalloc (per GPU)
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -81,6 +85,11 @@ def lib():
         L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, vp,
                                 ctypes.c_size_t, vp]
         L.fa_decode.restype = i
+        L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i,
+                                        vp]
+        L.fa_decode_noalloc.restype = i
+        L.fa_decode_noalloc_max_splits.argtypes = [i, i, i, i]
+        L.fa_decode_noalloc_max_splits.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -450,3 +459,34 @@ def fa_decode(q, k, v, scale=None, causal=False, window=0, seqlens_k=None,
         raise FaError(st, "fa_decode")
     return out, lse
 
+
+def fa_decode_noalloc_max_splits(B, Hq, Nq, d):
+    return int(lib().fa_decode_noalloc_max_splits(int(B), int(Hq), int(Nq), int(d)))
+
+
+def fa_decode_noalloc(q, k, v, out, lse, scale=None, causal=False, window=0, seqlens_k=None,
+                      num_splits=0, stream=None):
+    """fa_decode for callers that cannot allocate: the caller passes the
+    outputs (out bf16 like q, lse fp32 [B, Hq, Nq]) and the split partials go
+    to the library's static device scratch, so neither this wrapper nor the
+    library allocates.  num_splits = 0 picks the default count that fits.
+    Calls that overlap on one GPU race on the scratch."""
+    import torch
+    if out is None or lse is None:
+        raise ValueError("fa_decode_noalloc writes into caller-supplied out and lse")
+    B, hq, hkv, nq, nk, d = _geometry(q, k, v, None, None, torch.bfloat16)
+    if seqlens_k is not None:
+        _tensor("seqlens_k", seqlens_k, torch.int32, (B,))
+    _tensor("out", out, torch.bfloat16, q.shape)
+    _tensor("lse", lse, torch.float32, (B, hq, nq))
+    _same_device(q.device, [("q", q), ("k", k), ("v", v), ("seqlens_k", seqlens_k),
+                            ("out", out), ("lse", lse)])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = _launch_stream(stream)
+    st = lib().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, hq, hkv,
+                                 nq, nk, d, float(scale), int(bool(causal)), int(window),
+                                 _ptr(seqlens_k), int(num_splits), _stream_arg(s))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_noalloc")
+    return out, lse

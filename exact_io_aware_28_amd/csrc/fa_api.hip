@@ -2,11 +2,15 @@
 // validation, then dispatch to the kernel launchers.
 //
 // Validation touches no HIP API, so a rejected call enqueues nothing and the
-// checks can be exercised on a machine without a GPU.
+// checks can be exercised on a machine without a GPU.  (fa_decode_noalloc
+// asks the runtime for its scratch array's device address only after its
+// arguments have passed.)
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <climits>
+#include <mutex>
 
 #include "fa_mi355x.h"
 #include "fa_params.h"
@@ -307,45 +311,148 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
   return (int)(s < 1 ? 1 : s);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks and parameter block shared by fa_decode and fa_decode_noalloc;
+// `workspace` may still be null here (the no-allocation entry point fills
+// it in after the size check).
+int decode_prepare(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+                   const int32_t* seqlens_k, int num_splits, fa::DecodeParams* p) {
+  const void* t[] = {q, k, v, o};
+  const float* s[] = {lse};
+  int st = check_common(t, 4, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window, nullptr, 64);
+  if (st != FA_OK) return st;
+  if (seqlens_k && !aligned(seqlens_k, 4)) return FA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
+  const int64_t row_blocks = ((int64_t)(Hq / Hkv) * Nq + 31) / 32;
+  if ((int64_t)num_splits * row_blocks * Hkv * B > (int64_t)UINT32_MAX / 2)
+    return FA_ERR_UNSUPPORTED;
+  p->q = q;
+  p->k = k;
+  p->v = v;
+  p->o = o;
+  p->lse = lse;
+  p->seqlens_k = seqlens_k;
+  p->opart = nullptr;
+  p->lpart = nullptr;
+  p->B = B;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->Nq = Nq;
+  p->Nk = Nk;
+  p->d = d;
+  p->group = Hq / Hkv;
+  p->causal = causal;
+  p->window = window;
+  p->scale = scale;
+  p->scale_log2 = scale * 1.4426950408889634f;
+  p->num_splits = num_splits;
+  p->row_blocks = (int)row_blocks;
+  return FA_OK;
+}
+
+// The split partials inside a workspace: opart first, lpart after it.
+void decode_set_workspace(fa::DecodeParams* p, void* workspace) {
+  p->opart = static_cast<float*>(workspace);
+  p->lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      decode_opart_bytes(p->B, p->Hq, p->Nq, p->d,
+                                                         p->num_splits));
+}
+
+}  // namespace
+
+// ------------------------------------------------ allocation-free decode
+// fa_decode_noalloc keeps its split partials in this fixed device array
+// instead of a caller workspace.  Each GPU holds its own copy, at its own
+// address, from the library's load until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address of the copy on each GPU is looked up once, with that GPU current,
+// and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the
+// first call per device).
+int scratch_on_current_device(hipStream_t stream, void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+    if (sdev != dev) return FA_ERR_INVALID_ARG;  // the copy looked up must be the stream's
+  }
+  void* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    a = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!a) {
+      if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return FA_ERR_HIP;
+      g_scratch_addr[dev].store(a, std::memory_order_release);
+    }
+  }
+  *addr = a;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
               int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
               const int32_t* seqlens_k, int num_splits, void* workspace,
               size_t workspace_bytes, void* stream) {
-  const void* t[] = {q, k, v, o, workspace};
-  const float* s[] = {lse};
-  int st = check_common(t, 5, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window, nullptr,
-                        64);
+  fa::DecodeParams p;
+  int st = decode_prepare(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                          seqlens_k, num_splits, &p);
   if (st != FA_OK) return st;
-  if (seqlens_k && !aligned(seqlens_k, 4)) return FA_ERR_INVALID_ARG;
-  if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
   if (workspace_bytes < fa_decode_workspace_size(B, Hq, Nq, d, num_splits))
     return FA_ERR_INVALID_ARG;
-  const int64_t row_blocks = ((int64_t)(Hq / Hkv) * Nq + 31) / 32;
-  if ((int64_t)num_splits * row_blocks * Hkv * B > (int64_t)UINT32_MAX / 2)
-    return FA_ERR_UNSUPPORTED;
+  decode_set_workspace(&p, workspace);
+  return fa::launch_decode_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_noalloc_max_splits(int B, int Hq, int Nq, int d) {
+  if (B < 1 || Hq < 1 || Nq < 1 || d < 1) return 0;
+  int lo = 0;
+  for (int s = 1; s <= 1024; ++s) {
+    if (fa_decode_workspace_size(B, Hq, Nq, d, s) > (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES)
+      break;
+    lo = s;
+  }
+  return lo;
+}
+
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int window, const int32_t* seqlens_k, int num_splits, void* stream) {
+  if (num_splits == 0) {  // the default count, lowered until the partials fit
+    num_splits = fa_decode_num_splits(B, Hq, Hkv, Nq, Nk);
+    const int cap = fa_decode_noalloc_max_splits(B, Hq, Nq, d);
+    if (num_splits > cap) num_splits = cap;
+    if (num_splits < 1) return FA_ERR_TOO_LARGE;
+  }
   fa::DecodeParams p;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.lse = lse;
-  p.seqlens_k = seqlens_k;
-  p.opart = static_cast<float*>(workspace);
-  p.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                     decode_opart_bytes(B, Hq, Nq, d, num_splits));
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.Nq = Nq;
-  p.Nk = Nk;
-  p.d = d;
-  p.group = Hq / Hkv;
-  p.causal = causal;
-  p.window = window;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.num_splits = num_splits;
-  p.row_blocks = (int)row_blocks;
+  int st = decode_prepare(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
+                          seqlens_k, num_splits, &p);
+  if (st != FA_OK) return st;
+  if (fa_decode_workspace_size(B, Hq, Nq, d, num_splits) >
+      (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_TOO_LARGE;
+  void* addr = nullptr;
+  st = scratch_on_current_device((hipStream_t)stream, &addr);
+  if (st != FA_OK) return st;
+  decode_set_workspace(&p, addr);
   return fa::launch_decode_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -359,6 +466,9 @@ const char* fa_status_string(int status) {
       return "FA_ERR_UNSUPPORTED: unsupported configuration";
     case FA_ERR_HIP:
       return "FA_ERR_HIP: HIP runtime error";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: the request needs more scratch than the library's static "
+             "buffer holds (FA_DECODE_NOALLOC_SCRATCH_BYTES per device)";
     default:
       return "unknown fa_status";
   }

@@ -41,9 +41,10 @@
  *
  * Ownership and execution.  Every buffer is owned by the caller and lives in
  * device memory (HBM) unless stated otherwise.  The library never allocates,
- * frees or synchronises, and keeps no mutable global state: calls are thread
- * safe and only enqueue work on `stream` (a hipStream_t; NULL = the null
- * stream) before returning.  Inputs are read-only; outputs are fully
+ * frees or synchronises.  Its only global state is the static device scratch
+ * of fa_decode_noalloc and that array's per-device address, looked up once:
+ * calls are thread safe and only enqueue work on `stream` (a hipStream_t;
+ * NULL = the null stream) before returning.  Inputs are read-only; outputs are fully
  * overwritten, never accumulated into.  Results are deterministic: the same
  * inputs give the same bits.
  *
@@ -68,7 +69,9 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, bad scale */
   FA_ERR_UNSUPPORTED = 2,  /* valid request this library does not implement */
-  FA_ERR_HIP = 3           /* the HIP runtime rejected a launch */
+  FA_ERR_HIP = 3,          /* the HIP runtime rejected a launch */
+  FA_ERR_TOO_LARGE = 4     /* needs more than the static scratch of
+                              fa_decode_noalloc holds */
 } fa_status;
 
 /*
@@ -257,6 +260,34 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               float scale, int causal, int window,
               const int32_t* seqlens_k, int num_splits,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine): the split partials live in a
+ * static device array of FA_DECODE_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds from the library's load until the process ends.
+ *   Arguments as fa_decode, without workspace and workspace_bytes;
+ *   num_splits == 0 picks fa_decode_num_splits' count, lowered to
+ *   fa_decode_noalloc_max_splits so that the partials fit.
+ *   Returns FA_ERR_TOO_LARGE, before enqueueing anything, when the partials
+ *   of the request (fa_decode_workspace_size bytes) exceed the array;
+ *   FA_ERR_INVALID_ARG also when `stream` belongs to another device than the
+ *   current one.  The results are bit for bit those of fa_decode with the
+ *   same num_splits.
+ *   The array is shared by every call on a GPU and keeps the last call's
+ *   contents; nothing in it needs to start at zero (every partial a call
+ *   reads, the same call writes first).  Calls that overlap on one GPU (two
+ *   streams, or two host threads with work in flight at once) race on it
+ *   and corrupt each other's results: serialise them.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fa_decode_noalloc_max_splits(int B, int Hq, int Nq, int d);
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      float scale, int causal, int window,
+                      const int32_t* seqlens_k, int num_splits, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(int status);

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_dropout",
                                     "fa_bwd_workspace_size",
-                                    "fa_decode", "fa_decode_num_splits",
+                                    "fa_decode", "fa_decode_noalloc",
+                                    "fa_decode_noalloc_max_splits", "fa_decode_num_splits",
                                     "fa_decode_workspace_size", "fa_fwd", "fa_fwd_bias",
                                     "fa_fwd_dropout", "fa_fwd_f16", "fa_fwd_f32",
                                     "fa_status_string"]
@@ -170,6 +171,45 @@ def _dec(ws=P[9], ws_bytes=None, **kw):
 ])
 def test_decode_rejects(bad, code):
     assert _dec(**bad) == code
+
+
+def _dec_noalloc(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, Hq=8, Hkv=2, Nq=1, Nk=4096,
+             d=128, scale=0.125, causal=1, window=0, lens=None, splits=4)
+    a.update(kw)
+    return fa.lib().fa_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                      a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                      a["causal"], a["window"], a["lens"], a["splits"], None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    # partials of 8 splits x 64 x 16 x 64 rows x 128 floats: 256 MiB > 32 MiB
+    (dict(B=64, Hq=64, Hkv=8, Nq=16, splits=8), fa.FA_ERR_TOO_LARGE),
+    # even one split (32 MiB of partial outputs plus their LSEs) does not fit
+    (dict(B=64, Hq=64, Hkv=8, Nq=16, splits=0), fa.FA_ERR_TOO_LARGE),
+    (dict(splits=1025), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lens=ctypes.c_void_p(0x10002)), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+])
+def test_decode_noalloc_rejects_before_any_hip_call(bad, code):
+    assert _dec_noalloc(**bad) == code
+
+
+def test_decode_noalloc_max_splits():
+    cap = fa.DECODE_NOALLOC_SCRATCH_BYTES
+    # 16 sequences x 32 heads x 128 floats per split, plus 16 x 32 LSEs
+    assert fa.fa_decode_noalloc_max_splits(16, 32, 1, 128) == cap // (16 * 32 * 129 * 4)
+    for args in [(16, 32, 1, 128), (3, 8, 4, 64), (64, 32, 8, 128)]:
+        s = fa.fa_decode_noalloc_max_splits(*args)
+        assert fa.fa_decode_workspace_size(*args, s) <= cap
+        assert s == 1024 or fa.fa_decode_workspace_size(*args, s + 1) > cap
+    assert fa.fa_decode_noalloc_max_splits(64, 64, 16, 128) == 0
+    assert fa.fa_decode_noalloc_max_splits(0, 64, 16, 128) == 0
+    assert "FA_ERR_TOO_LARGE" in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
 
 
 def test_decode_workspace_and_default_splits():
