@@ -21,3 +21,4 @@ from .attention import (  # noqa: F401
 )
 from .online_recurrence import online_attention  # noqa: F401
 from .philox import drop_threshold, keep_mask, keep_scale, philox4x32_10  # noqa: F401
+from . import fp8  # noqa: F401,E402
