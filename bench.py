@@ -33,6 +33,7 @@ import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: twice the bf16 rate
 METRIC = "attention TFLOP/s + % of bf16 MFMA peak, causal fwd N=8192 d=128 GQA"
 # the forward kernel's sources and the build script that sets its code-generation
 # options (paths relative to the package's csrc/)
@@ -276,6 +277,47 @@ def time_decode(inp, steps, warmup):
     return timed(launch, steps, torch.cuda.current_stream())[0], splits
 
 
+def time_fp8(name, steps, warmup):
+    """FP8 forward over resident E4M3 codes and block scales, and the
+    quantizer that makes them from bf16 (Q and K rotated, V transposed)."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    inp = workloads.make_fp8_inputs(name)
+    dev8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().view(torch.float8_e4m3fn)
+    q8, k8 = dev8(inp["q8"]), dev8(inp["k8"])
+    vt8 = dev8(workloads.transpose_v8(inp["v8"]))
+    sq, sk, sv = (torch.from_numpy(inp[n]).cuda() for n in ("sq", "sk", "sv"))
+    o, lse = fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, causal=inp["causal"], window=inp["window"])
+    launch = lambda: fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, causal=inp["causal"],
+                                   window=inp["window"], out=o, lse=lse)
+    warm_up(launch, warmup)
+    ms = timed(launch, steps, torch.cuda.current_stream())[0]
+    flops = attention_flops(dict(inp, cu_seqlens=None))
+    # the quantizer over bf16 tensors of the same shapes
+    B, N, hq, hkv, d = inp["B"], inp["Nq"], inp["Hq"], inp["Hkv"], inp["d"]
+    xq = torch.randn(B, N, hq, d, device="cuda").to(torch.bfloat16)
+    xk = torch.randn(B, N, hkv, d, device="cuda").to(torch.bfloat16)
+    signs = (torch.randint(0, 2, (d,), device="cuda") * 2 - 1).float()
+    qo, qs = fa.fa_quantize_fp8(xq, signs=signs)
+    ko, ks = fa.fa_quantize_fp8(xk, signs=signs)
+    vo, vs = fa.fa_quantize_fp8(xk, transpose=True)
+
+    def quant():
+        fa.fa_quantize_fp8(xq, signs=signs, out=qo, scales=qs)
+        fa.fa_quantize_fp8(xk, signs=signs, out=ko, scales=ks)
+        fa.fa_quantize_fp8(xk, transpose=True, out=vo, scales=vs)
+    warm_up(quant, warmup)
+    qms = timed(quant, steps, torch.cuda.current_stream())[0]
+    # bytes moved: each bf16 element read (2 B) and its code written (1 B)
+    qbytes = 3 * xq.numel() + 2 * 3 * xk.numel()
+    return {"workload": name, "direction": "fwd", "dtype": "fp8-e4m3", "ms": round(ms, 4),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_fp8_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "quantize_qkv_ms": round(qms, 4),
+            "quantize_GB/s": round(qbytes / (qms * 1e-3) / 1e9, 1)}
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size, for scaling the HBM
     counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
@@ -395,6 +437,9 @@ def main(argv=None):
               flush=True)
         del wd
         torch.cuda.empty_cache()
+        for name in workloads.FP8_WORKLOADS:
+            print(json.dumps(time_fp8(name, max(a.steps, 10), a.warmup)), flush=True)
+            torch.cuda.empty_cache()
         for name in workloads.DECODE_WORKLOADS:
             di = workloads.make_decode_inputs(name)
             dms, splits = time_decode(di, max(a.steps, 10), a.warmup)

@@ -18,6 +18,8 @@ Functions mirror the C ABI in include/fa_mi355x.h:
     fa_decode_num_splits(B, Hq, Hkv, Nq, Nk) -> int
     fa_decode_noalloc(q, k, v, out, lse, ...) -> (out, lse), no allocation
     fa_decode_noalloc_max_splits(B, Hq, Nq, d) -> int
+    fa_quantize_fp8(x, signs, transpose) -> (x8 float8_e4m3fn, scales)
+    fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, ...) -> (o bf16, lse)
     fa_status_string(status) -> str
 """
 
@@ -90,6 +92,10 @@ def lib():
         L.fa_decode_noalloc.restype = i
         L.fa_decode_noalloc_max_splits.argtypes = [i, i, i, i]
         L.fa_decode_noalloc_max_splits.restype = i
+        L.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp]
+        L.fa_quantize_fp8.restype = i
+        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.fa_fwd_fp8.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -489,4 +495,83 @@ def fa_decode_noalloc(q, k, v, out, lse, scale=None, causal=False, window=0, seq
                                  _ptr(seqlens_k), int(num_splits), _stream_arg(s))
     if st != FA_OK:
         raise FaError(st, "fa_decode_noalloc")
+    return out, lse
+
+
+# ------------------------------------------------------------------ FP8
+FP8_BLOCK = 64  # tokens per scale block
+
+
+def _fp8(name, t, shape):
+    """An E4M3 code tensor (torch.float8_e4m3fn or raw uint8 bytes)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"{name} must be a float8_e4m3fn (or uint8) tensor")
+    return _tensor(name, t, t.dtype, shape)
+
+
+def fa_quantize_fp8(x, signs=None, transpose=False, out=None, scales=None, stream=None):
+    """Block-quantize bf16 x [B, N, H, d] to E4M3 (one fp32 scale per 64
+    tokens of one head), optionally rotating each row by x D H / sqrt(d)
+    first (signs: device fp32 [d] of +-1).  Returns (x8, scales): x8 is
+    float8_e4m3fn [B, N, H, d], or [B, H, d, ldn] (ldn = N rounded up to 64,
+    zero padded) with transpose=True, the layout fa_fwd_fp8 takes for V."""
+    import torch
+    _tensor("x", x, torch.bfloat16)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, N, H, d]")
+    B, N, H, d = x.shape
+    nb = -(-N // FP8_BLOCK)
+    shape = (B, H, d, nb * FP8_BLOCK) if transpose else (B, N, H, d)
+    if out is not None:
+        _fp8("out", out, shape)
+    _optional("scales", scales, torch.float32, (B, H, nb))
+    if signs is not None:
+        _tensor("signs", signs, torch.float32, (d,))
+    _same_device(x.device, [("x", x), ("out", out), ("scales", scales), ("signs", signs)])
+    s = _launch_stream(stream)
+    out = _alloc(out, shape, torch.float8_e4m3fn, s, x.device)
+    scales = _alloc(scales, (B, H, nb), torch.float32, s, x.device)
+    st = lib().fa_quantize_fp8(_ptr(x), _ptr(out), _ptr(scales), B, N, H, d, int(bool(transpose)),
+                               _ptr(signs), _stream_arg(s))
+    if st != FA_OK:
+        raise FaError(st, "fa_quantize_fp8")
+    return out, scales
+
+
+def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, scale=None, causal=False, window=0,
+               out=None, lse=None, stream=None):
+    """FP8 forward over E4M3 codes with block scales (see
+    include/fa_mi355x.h): q8 [B, Nq, Hq, d], k8 [B, Nk, Hkv, d], vt8
+    [B, Hkv, d, ldv] (ldv = Nk rounded up to 64), scales [B, H, ceil(N/64)].
+    Returns (o bf16 [B, Nq, Hq, d], lse fp32 [B, Hq, Nq])."""
+    import torch
+    for name, t in (("q8", q8), ("k8", k8), ("vt8", vt8)):
+        _fp8(name, t, None)
+    if q8.dim() != 4 or k8.dim() != 4 or vt8.dim() != 4:
+        raise ValueError("q8, k8 must be [B, N, H, d] and vt8 [B, Hkv, d, ldv]")
+    B, nq, hq, d = q8.shape
+    nk, hkv = k8.shape[1], k8.shape[2]
+    if k8.shape[0] != B or k8.shape[3] != d:
+        raise ValueError(f"k8 {tuple(k8.shape)} does not match q8 {tuple(q8.shape)}")
+    ldv = -(-nk // FP8_BLOCK) * FP8_BLOCK
+    _fp8("vt8", vt8, (B, hkv, d, ldv))
+    _tensor("q_scale", q_scale, torch.float32, (B, hq, -(-nq // FP8_BLOCK)))
+    _tensor("k_scale", k_scale, torch.float32, (B, hkv, -(-nk // FP8_BLOCK)))
+    _tensor("v_scale", v_scale, torch.float32, (B, hkv, -(-nk // FP8_BLOCK)))
+    _optional("out", out, torch.bfloat16, (B, nq, hq, d))
+    _optional("lse", lse, torch.float32, (B, hq, nq))
+    _same_device(q8.device, [("q8", q8), ("k8", k8), ("vt8", vt8), ("q_scale", q_scale),
+                             ("k_scale", k_scale), ("v_scale", v_scale), ("out", out),
+                             ("lse", lse)])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = _launch_stream(stream)
+    out = _alloc(out, (B, nq, hq, d), torch.bfloat16, s, q8.device)
+    lse = _alloc(lse, (B, hq, nq), torch.float32, s, q8.device)
+    st = lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(q_scale), _ptr(k_scale),
+                          _ptr(v_scale), _ptr(out), _ptr(lse), B, hq, hkv, nq, nk, d,
+                          float(scale), int(bool(causal)), int(window), _stream_arg(s))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
     return out, lse

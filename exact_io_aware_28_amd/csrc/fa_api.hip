@@ -456,6 +456,68 @@ int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, floa
   return fa::launch_decode_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_quantize_fp8(const void* x, void* x8, float* scales, int B, int N, int H, int d,
+                    int transpose, const float* signs, void* stream) {
+  if (!x || !x8 || !scales || !aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4))
+    return FA_ERR_INVALID_ARG;
+  if (signs && !aligned(signs, 4)) return FA_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || H < 1 || d < 1 || (transpose != 0 && transpose != 1))
+    return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const int64_t nb = ((int64_t)N + 63) / 64;
+  if ((int64_t)B * H * nb > (int64_t)INT32_MAX) return FA_ERR_UNSUPPORTED;
+  fa::QuantParams p;
+  p.x = x;
+  p.x8 = static_cast<uint8_t*>(x8);
+  p.scales = scales;
+  p.signs = signs;
+  p.B = B;
+  p.N = N;
+  p.H = H;
+  p.d = d;
+  p.transpose = transpose;
+  p.ldn = (int)(nb * 64);
+  p.nb = (int)nb;
+  return fa::launch_quantize_fp8(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_scale,
+               const float* k_scale, const float* v_scale, void* o, float* lse, int B, int Hq,
+               int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+               void* stream) {
+  const void* t[] = {q8, k8, vt8, o};
+  const float* s[] = {lse, q_scale, k_scale, v_scale};
+  int st = check_common(t, 4, s, 4, B, Hq, Hkv, Nq, Nk, d, scale, causal, window, nullptr, 64);
+  if (st != FA_OK) return st;
+  const int64_t ldv = ((int64_t)Nk + 63) / 64 * 64;
+  // the V^T tile's buffer descriptor spans d - 1 rows of ldv bytes plus one tile row
+  if ((int64_t)(d - 1) * ldv + 64 >= ((int64_t)1 << 32)) return FA_ERR_UNSUPPORTED;
+  fa::Fp8FwdParams p;
+  p.q = static_cast<const uint8_t*>(q8);
+  p.k = static_cast<const uint8_t*>(k8);
+  p.v = static_cast<const uint8_t*>(vt8);
+  p.sq = q_scale;
+  p.sk = k_scale;
+  p.sv = v_scale;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.group = Hq / Hkv;
+  p.causal = causal;
+  p.window = window;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.num_qtiles = 0;
+  p.ldv = (int)ldv;
+  p.nbq = (Nq + 63) / 64;
+  p.nbk = (Nk + 63) / 64;
+  return fa::launch_fwd_fp8(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK:

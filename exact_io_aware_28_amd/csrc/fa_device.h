@@ -144,6 +144,42 @@ __host__ __device__ constexpr int tile_off(int r, int col) {
   return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
 }
 
+// ---------------------------------------------------------------- 8-bit tiles
+// The FP8 forward stages two byte tiles per key block:
+//   * K: 64 rows (keys) of D bytes;
+//   * V^T: D rows (head-dimension columns) of 64 bytes (keys).
+// Both are stored with their 16-byte chunks permuted inside each row (chunk c
+// of row r at chunk c ^ swz(r)); the permutations are checked exhaustively on
+// the host, for 32- and 64-bank LDS, against the reads the kernel issues:
+//   * K: lane (m, h) of a wave (m = lane % 32, h = lane / 32) reads 16 bytes
+//     at row k8_row(kb, m), chunk 4 st + 2 h + u (D = 128) or 2 h + u
+//     (D = 64), for key block kb, k-step st and half u of its 32 bytes;
+//   * V^T: lane (m, h) reads 16 bytes at row 32 db + m, chunk 2 h + u.
+template <int D>
+__host__ __device__ constexpr int swz_k8(int r) {
+  if constexpr (D == 128)  // bits (r0 ^ r2, r1, r5) of the row
+    return ((r ^ (r >> 2)) & 1) | (((r >> 1) & 1) << 1) | (((r >> 5) & 1) << 2);
+  else  // 4 chunks: bits (r1 ^ r2, r5)
+    return (((r >> 1) ^ (r >> 2)) & 1) | (((r >> 5) & 1) << 1);
+}
+__host__ __device__ constexpr int swz_v8(int r) {  // 4 chunks: bits (r1 ^ r3, r2)
+  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
+}
+template <int D>
+__host__ __device__ constexpr int k8_off(int r, int byte) {
+  return r * D + ((((byte >> 4) ^ swz_k8<D>(r))) << 4) + (byte & 15);
+}
+__host__ __device__ constexpr int v8_off(int r, int byte) {
+  return r * 64 + ((((byte >> 4) ^ swz_v8(r))) << 4) + (byte & 15);
+}
+// K-tile row read by A-operand row m of key block kb in the FP8 score
+// product.  With this order the 32 x 32 result gives lane half h the scores
+// of the 32 consecutive keys 32 h + 16 kb + i (i = 0..15), which is the
+// order the P V product takes them in: P never needs a permutation.
+__host__ __device__ constexpr int k8_row(int kb, int m) {
+  return 32 * ((m >> 2) & 1) + 16 * kb + 4 * (m >> 3) + (m & 3);
+}
+
 // LDS reads at a lane byte offset plus a byte offset that is a compile-time
 // constant after unrolling (whole rows, or a tile).  Keeping the lane part
 // in one register and the rest constant lets every read of a tile reuse that

@@ -83,6 +83,38 @@ struct DecodeParams {
   int row_blocks;             // ceil(group * Nq / 32)
 };
 
+// One FP8 forward call (dense batches), already validated.  Codes are OCP
+// E4M3 bytes; every block of 64 tokens of one head has one fp32 scale.
+struct Fp8FwdParams {
+  const uint8_t* q;           // [B, Nq, Hq, d]
+  const uint8_t* k;           // [B, Nk, Hkv, d]
+  const uint8_t* v;           // V transposed: [B, Hkv, d, ldv], keys innermost
+  const float* sq;            // [B, Hq, nbq]
+  const float* sk;            // [B, Hkv, nbk]
+  const float* sv;            // [B, Hkv, nbk]
+  void* o;                    // bf16 [B, Nq, Hq, d]
+  float* lse;                 // [B, Hq, Nq]
+  int B, Hq, Hkv, Nq, Nk, d;
+  int group;
+  int causal, window;
+  float scale_log2;           // scale * log2(e)
+  int num_qtiles;             // set by the launcher
+  int ldv;                    // keys per V^T row: Nk rounded up to 64
+  int nbq, nbk;               // scale blocks per head: ceil(Nq / 64), ceil(Nk / 64)
+};
+
+// One block quantization call (bf16 -> E4M3 codes and block scales).
+struct QuantParams {
+  const void* x;              // bf16 [B, N, H, d]
+  uint8_t* x8;                // [B, N, H, d], or [B, H, d, ldn] when transposed
+  float* scales;              // [B, H, nb]
+  const float* signs;         // d values of +-1 (rotation), or nullptr
+  int B, N, H, d;
+  int transpose;              // write the V^T layout
+  int ldn;                    // N rounded up to 64 (row length of the V^T layout)
+  int nb;                     // ceil(N / 64)
+};
+
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
@@ -91,5 +123,7 @@ hipError_t launch_fwd_d128(const FwdParams& p, hipStream_t stream, bool f16);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
+hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t stream);
 
 }  // namespace fa

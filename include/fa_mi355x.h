@@ -289,6 +289,58 @@ int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, floa
                       float scale, int causal, int window,
                       const int32_t* seqlens_k, int num_splits, void* stream);
 
+/*
+ * FP8 forward (llms.blog "FlashAttention: How IO-Aware Tiling and Online
+ * Softmax Solved Transformer Memory Bottlenecks", "FlashAttention-3:
+ * Asynchronous Execution on Hopper Architectures": 8-bit floating point with
+ * block quantization and incoherent processing).  Dense batches only.
+ *
+ * Codes are OCP FP8 E4M3 bytes (bias 7, 3 mantissa bits, largest finite
+ * 448, S.1111.111 NaN).  Every block of 64 consecutive tokens of one head
+ * (all d columns) has one fp32 scale; the value of a code c of token n is
+ * e4m3(c) * scale[b, h, n / 64].
+ *
+ * fa_quantize_fp8: block quantization of a bf16 tensor.
+ *   x         : bf16 [B, N, H, d]
+ *   signs     : NULL, or device fp32[d] of +1 / -1: each row is first rotated
+ *               to x D H / sqrt(d) (D = diag(signs), H the Sylvester-
+ *               Hadamard matrix, H[i][j] = (-1)^popcount(i & j)); pass the
+ *               same signs for Q and K (the scores are unchanged, an outlier
+ *               coordinate is spread over the row), none for V
+ *   transpose : 0 -> x8 is [B, N, H, d] (the layout of Q and K);
+ *               1 -> x8 is [B, H, d, ldn], ldn = N rounded up to 64, keys
+ *               innermost, padding written as zeros (the layout V takes)
+ *   scales    : fp32 output [B, H, ceil(N / 64)]
+ * Per block, in fp32: amax = max |x| (after the rotation), scale = amax / 448,
+ * code = RNE_e4m3(clamp(x * (448 / amax), -448, 448)); a block with
+ * amax < 2^-119 gets scale 1 and zero codes.  NaN inputs give NaN codes.
+ * x, x8 16-byte aligned, scales and signs 4-byte aligned.  Errors:
+ * FA_ERR_INVALID_ARG (null or misaligned pointer, size < 1, transpose not 0
+ * or 1), FA_ERR_UNSUPPORTED (d not 64 or 128).
+ *
+ * fa_fwd_fp8: attention of the quantized problem,
+ *   S = scale * (sQ Q~)(sK K~)^T (+ causal / window masks),
+ *   O = softmax(S) (sV V~) in bf16, LSE as fa_fwd.
+ *   q8        : E4M3 [B, Nq, Hq, d];  k8 : E4M3 [B, Nk, Hkv, d]
+ *   vt8       : E4M3 [B, Hkv, d, ldv], ldv = Nk rounded up to 64 (what
+ *               fa_quantize_fp8 writes with transpose = 1); the padding keys
+ *               must hold finite codes (zeros)
+ *   q_scale   : fp32 [B, Hq, ceil(Nq / 64)];  k_scale, v_scale : fp32
+ *               [B, Hkv, ceil(Nk / 64)]; positive and finite
+ *   o         : bf16 [B, Nq, Hq, d];  lse : fp32 [B, Hq, Nq]
+ * Both products run on the 8-bit matrix cores, so the probabilities are
+ * rounded to E4M3 before they multiply V (relative error <= 2^-4 of each
+ * term of O); the row normaliser and LSE use the unrounded values.  Other
+ * arguments, masks and errors as fa_fwd (no packed batches), plus
+ * FA_ERR_UNSUPPORTED when (d - 1) * ldv + 64 >= 2^32.
+ */
+int fa_quantize_fp8(const void* x, void* x8, float* scales, int B, int N, int H, int d,
+                    int transpose, const float* signs, void* stream);
+int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_scale,
+               const float* k_scale, const float* v_scale, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               float scale, int causal, int window, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(int status);
 

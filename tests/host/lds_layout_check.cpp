@@ -66,10 +66,70 @@ int check() {
   return bad;
 }
 
+// The 8-bit tiles of the FP8 forward (fa_device.h, "8-bit tiles"): both
+// swizzles permute each row's chunks, the K-tile row order k8_row covers every
+// key once per key block, and the 128-bit reads of a wave are conflict-free.
+template <int D>
+int check_fp8() {
+  int bad = 0;
+  constexpr int kChunksK = D / 16;
+  for (int r = 0; r < 64; ++r) {
+    std::set<int> ck, cv;
+    for (int c = 0; c < kChunksK; ++c) ck.insert(fa::k8_off<D>(r, 16 * c) - r * D);
+    for (int c = 0; c < 4; ++c) cv.insert(fa::v8_off(r, 16 * c) - r * 64);
+    if ((int)ck.size() != kChunksK || (int)cv.size() != 4) {
+      std::printf("fp8 D=%d row %d: swizzle is not a permutation\n", D, r);
+      ++bad;
+    }
+  }
+  for (int kb = 0; kb < 2; ++kb) {
+    std::set<int> rows;
+    for (int m = 0; m < 32; ++m) rows.insert(fa::k8_row(kb, m));
+    for (int h = 0; h < 2; ++h)
+      for (int i = 0; i < 16; ++i) {  // result row 8(i/4) + 4h + i%4 holds key 32h + 16kb + i
+        const int m = 8 * (i / 4) + 4 * h + (i % 4);
+        if (fa::k8_row(kb, m) != 32 * h + 16 * kb + i) {
+          std::printf("fp8 k8_row(%d, %d) != %d\n", kb, m, 32 * h + 16 * kb + i);
+          ++bad;
+        }
+      }
+    if ((int)rows.size() != 32) ++bad;
+  }
+  for (int model = 0; model < 2; ++model) {
+    const int nbanks = model ? 64 : 32;
+    const int group = nbanks * 4 / 16;  // lanes served per pass by 128-bit reads
+    int k_conf = 0, v_conf = 0;
+    for (int kb = 0; kb < 2; ++kb)
+      for (int st = 0; st < D / 64; ++st)
+        for (int u = 0; u < 2; ++u)
+          for (int l0 = 0; l0 < 64; l0 += group) {
+            std::vector<int> a;
+            for (int l = l0; l < l0 + group; ++l) {
+              const int m = l % 32, h = l / 32;
+              const int chunk = (D == 128 ? 4 * st : 0) + 2 * h + u;
+              a.push_back(fa::k8_off<D>(fa::k8_row(kb, m), 16 * chunk));
+            }
+            k_conf += conflicts(a, 16, nbanks);
+          }
+    for (int db = 0; db < D / 32; ++db)
+      for (int u = 0; u < 2; ++u)
+        for (int l0 = 0; l0 < 64; l0 += group) {
+          std::vector<int> a;
+          for (int l = l0; l < l0 + group; ++l)
+            a.push_back(fa::v8_off(32 * db + l % 32, 16 * (2 * (l / 32) + u)));
+          v_conf += conflicts(a, 16, nbanks);
+        }
+    std::printf("fp8 D=%d banks=%d: K b128 conflicts %d, V^T b128 conflicts %d\n", D, nbanks,
+                k_conf, v_conf);
+    bad += k_conf + v_conf;
+  }
+  return bad;
+}
+
 }  // namespace
 
 int main() {
-  const int bad = check<128>() + check<64>();
+  const int bad = check<128>() + check<64>() + check_fp8<128>() + check_fp8<64>();
   std::printf(bad ? "FAIL\n" : "OK\n");
   return bad ? 1 : 0;
 }

@@ -35,7 +35,7 @@ def test_header_declares_expected_entry_points():
                                     "fa_decode_noalloc_max_splits", "fa_decode_num_splits",
                                     "fa_decode_workspace_size", "fa_fwd", "fa_fwd_bias",
                                     "fa_fwd_dropout", "fa_fwd_f16", "fa_fwd_f32",
-                                    "fa_status_string"]
+                                    "fa_fwd_fp8", "fa_quantize_fp8", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():

@@ -1,0 +1,251 @@
+"""GPU parity of the FP8 path (fa_quantize_fp8, fa_fwd_fp8) against the
+fp64 oracle (oracle/fp8.py).
+
+Quantizer: codes and scales are integer / bit decisions taken in fp32 on
+both sides, so without the rotation they must match bit for bit, in both
+layouts.  With the rotation the two sides round the rotated values
+differently (fp32 butterflies against an fp64 product rounded to fp32), so
+a code may sit one E4M3 step away where the value lies on a rounding
+boundary: the decoded values must agree within one step and differ in
+fewer than 1 in 1000 codes, and the scales to 1e-6.
+
+Attention: the oracle is exact attention (fp64) of the dequantized inputs.
+The kernel rounds each probability to E4M3 (relative error <= 2^-4) before
+the P V product and O to bf16, so each element must satisfy
+    |O - O_exact| <= 2^-4 sum_j p_ij |V_jd| + 2^-8 |O_exact| + 1e-4,
+the mean error must stay within 1.5x that of the oracle's error model (P
+rounded to E4M3 relative to the row maximum) plus bf16's output rounding,
+and LSE, which uses the
+unrounded probabilities, must meet the 1e-3 bar.  Inputs are drawn directly
+as E4M3 codes with per-block scales (workloads.make_fp8_inputs).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import fp8 as F
+from tests.gpu_util import say, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_28_amd as fa
+    fa.lib()
+
+
+def _dev(x, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return (t if dtype is None else t.to(dtype)).cuda()
+
+
+def _codes(t):
+    import torch
+    return t.view(torch.uint8).cpu().numpy()
+
+
+# ------------------------------------------------------------ quantizer
+QUANT_CASES = [
+    # B, N, H, d
+    (1, 64, 1, 128),
+    (2, 150, 3, 64),      # ragged last block
+    (1, 333, 4, 128),
+    (1, 1, 2, 64),        # one token
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[f"q{i}" for i in range(len(QUANT_CASES))])
+def test_quantize_bit_exact(case):
+    import torch
+    import exact_io_aware_28_amd as fa
+    B, N, H, d = case
+    inp = workloads.make_inputs(dict(B=B, N=N, Hq=H, Hkv=H, d=d, seed=500 + N))
+    x = inp["q"] * (2.0 ** np.arange(H) / 4)[None, None, :, None].astype(np.float32)
+    x = workloads.round_bf16(x)
+    if N >= 128:
+        x[0, 64:128, 0] = 0.0  # an all-zero block: scale 1, zero codes
+    say(f"[fp8 quantize] B={B} N={N} H={H} d={d}")
+    ref_codes, ref_scales = F.quantize_blocks(x)
+    xt = _dev(x, torch.bfloat16)
+    c8, sc = fa.fa_quantize_fp8(xt)
+    ct8, sct = fa.fa_quantize_fp8(xt, transpose=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(sc.cpu().numpy(), ref_scales)
+    assert np.array_equal(sct.cpu().numpy(), ref_scales)
+    got = _codes(c8)
+    bad = np.flatnonzero(got != ref_codes)
+    assert bad.size == 0, (bad[:8], got.reshape(-1)[bad[:8]], ref_codes.reshape(-1)[bad[:8]])
+    assert np.array_equal(_codes(ct8), workloads.transpose_v8(ref_codes))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantize_rotated(d):
+    import torch
+    import exact_io_aware_28_amd as fa
+    B, N, H = 2, 200, 3
+    inp = workloads.make_inputs(dict(B=B, N=N, Hq=H, Hkv=H, d=d, seed=510 + d))
+    x = inp["q"].copy()
+    x[0, 3, 1, 5] = 60.0  # an outlier coordinate
+    x = workloads.round_bf16(x)
+    signs = np.where(np.random.default_rng(511).random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+    say(f"[fp8 quantize rotated] B={B} N={N} H={H} d={d}")
+    ref_codes, ref_scales = F.quantize_blocks(x, signs)
+    c8, sc = fa.fa_quantize_fp8(_dev(x, torch.bfloat16), signs=_dev(signs))
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    assert np.all(np.abs(sc / ref_scales - 1) <= 1e-6)
+    got, ref = F.e4m3_decode(_codes(c8)), F.e4m3_decode(ref_codes)
+    step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -6))) - 3),
+                      2.0 ** -9)
+    assert np.all(np.abs(got - ref) <= step * (1 + 1e-9))
+    frac = float((got != ref).mean())
+    say(f"  codes one step apart: {frac:.2e}")
+    assert frac < 1e-3
+
+
+# ------------------------------------------------------------ attention
+def _fp8_dev(inp):
+    import torch
+    return (_dev(inp["q8"]).view(torch.float8_e4m3fn), _dev(inp["k8"]).view(torch.float8_e4m3fn),
+            _dev(workloads.transpose_v8(inp["v8"])).view(torch.float8_e4m3fn),
+            _dev(inp["sq"]), _dev(inp["sk"]), _dev(inp["sv"]))
+
+
+def _probs(q, k, scale, rows, nq, causal, window):
+    """Exact probabilities of rows `rows` (for the error bound)."""
+    s = scale * (q @ k.T)
+    ok = oracle.allowed_mask(nq, len(k), causal, window)[rows]
+    s = np.where(ok, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    return np.where(l > 0, p / np.where(l > 0, l, 1.0), 0.0)
+
+
+def _check_rows(o, ref, p, vd, what):
+    """Per-element bound of the 8-bit P V product; returns mean |err|."""
+    err = np.abs(o - ref)
+    bound = 2.0 ** -4 * (p @ np.abs(vd)) + 2.0 ** -8 * np.abs(ref) + 1e-4
+    assert np.all(np.isfinite(o)), what
+    worst = float((err / bound).max())
+    assert worst <= 1.0, (what, worst)
+    return err
+
+
+CASES = [
+    # B, Nq, Nk, Hq, Hkv, d, causal, window
+    (1, 300, 300, 4, 2, 128, True, 0),
+    (2, 257, 257, 4, 4, 64, False, 0),
+    (1, 100, 300, 4, 2, 128, True, 0),     # chunked prefill (bottom-right)
+    (1, 333, 333, 8, 1, 128, True, 70),    # MQA, window
+    (1, 64, 64, 2, 1, 64, True, 0),        # one exact tile
+    (1, 300, 100, 2, 1, 128, True, 0),     # rows that see no key
+    (1, 1, 1, 1, 1, 128, False, 0),
+    (1, 520, 520, 2, 2, 128, False, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_fwd_fp8_parity(case):
+    import torch
+    import exact_io_aware_28_amd as fa
+    B, Nq, Nk, Hq, Hkv, d, causal, window = case
+    inp = workloads.make_fp8_inputs(dict(B=B, Nq=Nq, Nk=Nk, Hq=Hq, Hkv=Hkv, d=d, causal=causal,
+                                         window=window, seed=600 + Nq + Nk))
+    what = f"B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} window={window}"
+    say(f"[fp8 fwd] {what}")
+    q8, k8, vt8, sq, sk, sv = _fp8_dev(inp)
+    o, lse = fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, scale=inp["scale"], causal=causal,
+                           window=window)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    args = (inp["q8"], inp["k8"], inp["v8"], inp["sq"], inp["sk"], inp["sv"], inp["scale"],
+            causal, window)
+    o_ref, lse_ref = F.attn_fwd_fp8(*args)
+    o_model = F.attn_fwd_fp8_p_rounded(*args)
+    qd, kd, vd = (F.dequantize(inp[n], inp[s]) for n, s in (("q8", "sq"), ("k8", "sk"),
+                                                               ("v8", "sv")))
+    errs = []
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            p = _probs(qd[b, :, h], kd[b, :, g], inp["scale"], np.arange(Nq), Nq, causal,
+                       window)
+            errs.append(_check_rows(o[b, :, h], o_ref[b, :, h], p, vd[b, :, g], what))
+    err = np.concatenate([e.reshape(-1) for e in errs])
+    model = np.abs(o_model - o_ref)
+    say(f"  O max|err|={err.max():.3e} mean|err|={err.mean():.3e} "
+        f"(E4M3-P model: max {model.max():.3e} mean {model.mean():.3e})")
+    # the model has no output rounding: allow bf16's (half a step, 2^-9 |O|)
+    assert err.mean() <= 1.5 * model.mean() + 2.0 ** -9 * np.abs(o_ref).mean() + 1e-4
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref))
+    lerr = float(np.abs(lse[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+    say(f"  LSE max|err|={lerr:.3e}")
+    assert lerr <= 1e-3
+    assert np.all(o[~np.isfinite(lse_ref).reshape(B, Hq, Nq).transpose(0, 2, 1)] == 0)
+
+
+def test_fwd_fp8_gqa_prefill_sampled():
+    """The GQA causal prefill shape (B=1, Hq=32, Hkv=8, N=8192, d=128) in
+    FP8: sampled rows of every head against the oracle, in the launch
+    configuration the benchmark times."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    inp = workloads.make_fp8_inputs("gqa_causal_prefill_fp8")
+    say("[fp8 fwd] gqa_causal_prefill_fp8 B=1 Hq=32 Hkv=8 N=8192 d=128 causal")
+    q8, k8, vt8, sq, sk, sv = _fp8_dev(inp)
+    o, lse = fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, scale=inp["scale"], causal=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    rows = sample_rows(8192, count=12, seed=7)
+    lerr, errs = 0.0, []
+    for h in range(32):
+        g = h // 4
+        qd = F.dequantize(inp["q8"][:, :, h:h + 1], inp["sq"][:, h:h + 1])[0, :, 0]
+        kd = F.dequantize(inp["k8"][:, :, g:g + 1], inp["sk"][:, g:g + 1])[0, :, 0]
+        vd = F.dequantize(inp["v8"][:, :, g:g + 1], inp["sv"][:, g:g + 1])[0, :, 0]
+        ro, rl = oracle.attn_fwd_rows(qd, kd, vd, rows, inp["scale"], True, 0)
+        p = _probs(qd[rows], kd, inp["scale"], rows, 8192, True, 0)
+        errs.append(_check_rows(o[0, rows, h], ro, p, vd, f"head {h}"))
+        lerr = max(lerr, float(np.abs(lse[0, h, rows] - rl).max()))
+    err = np.concatenate([e.reshape(-1) for e in errs])
+    say(f"  O max|err|={err.max():.3e} mean|err|={err.mean():.3e} LSE max|err|={lerr:.3e}")
+    assert lerr <= 1e-3
+
+
+def test_quantize_then_attend_matches_bf16_attention():
+    """End to end: bf16 Q, K, V quantized on the GPU (Q and K rotated with the
+    same signs) and attended in FP8 land within the FP8 bound of the exact
+    bf16 attention, plus the quantization error of the inputs."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    inp = workloads.make_inputs(dict(B=1, N=400, Hq=4, Hkv=2, d=128, causal=True, seed=700))
+    say("[fp8 end to end] B=1 N=400 Hq=4 Hkv=2 d=128 causal, rotated Q/K")
+    signs = np.where(np.random.default_rng(701).random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+    dq, dk, dv = (_dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    sg = _dev(signs)
+    q8, sq = fa.fa_quantize_fp8(dq, signs=sg)
+    k8, sk = fa.fa_quantize_fp8(dk, signs=sg)
+    vt8, sv = fa.fa_quantize_fp8(dv, transpose=True)
+    o, lse = fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, causal=True)
+    torch.cuda.synchronize()
+    f = lambda n: inp[n].astype(np.float64)
+    o_ref, lse_ref = oracle.attn_fwd(f("q"), f("k"), f("v"), inp["scale"], True)
+    err = np.abs(o.float().cpu().numpy() - o_ref)
+    lerr = float(np.abs(lse.cpu().numpy() - lse_ref).max())
+    say(f"  vs bf16 attention: O max|err|={err.max():.3e} mean|err|={err.mean():.3e} "
+        f"LSE max|err|={lerr:.3e}")
+    # inputs carry E4M3's 2^-4 relative error too: scores move by ~2^-4 of
+    # |q||k| scale at worst, so only coarse bars apply here
+    assert err.mean() < 0.03 and err.max() < 0.35 and lerr < 0.2

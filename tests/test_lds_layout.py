@@ -25,3 +25,4 @@ def test_swizzle_is_a_permutation_and_bank_conflict_free(tmp_path):
     assert run.returncode == 0, run.stdout
     assert run.stdout.strip().endswith("OK")
     assert run.stdout.count("conflicts 0, tr_b16 conflicts 0") == 4
+    assert run.stdout.count("K b128 conflicts 0, V^T b128 conflicts 0") == 4

@@ -53,6 +53,14 @@ WORKLOADS = {
 }
 
 
+# 8-bit workloads: E4M3 codes with one fp32 scale per 64 tokens of one head.
+FP8_WORKLOADS = {
+    # the GQA causal prefill shape with FP8 Q, K, V
+    "gqa_causal_prefill_fp8": dict(B=1, Hq=32, Hkv=8, N=8192, d=128, causal=True, window=0,
+                                   seed=9),
+}
+
+
 # Decode over a key/value cache (few new query rows per sequence, long cache).
 #   kv_lengths: keys in use per sequence, drawn uniformly from [Lmin, Lmax]
 #   Nk: cache capacity per sequence (rows past a sequence's length are unused)
@@ -184,4 +192,62 @@ def make_decode_inputs(spec, seed=None):
         out["bias"] = draw_bias(rng, spec["bias_shape"], out, spec.get("bias_masked", 0.1))
     out["scale"] = spec.get("scale", 1.0 / math.sqrt(d))
     out["dtype"] = "bf16"
+    return out
+
+
+def e4m3_codes(x):
+    """float32 values -> OCP E4M3 codes (uint8), by torch's float8_e4m3fn
+    cast (nearest even); values must lie within +-448."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def make_fp8_inputs(spec, seed=None):
+    """Draw an 8-bit workload directly in its quantized form: codes of
+    N(0, 1) * 112 (clipped to +-448) cast to E4M3 for Q, K and V (V in
+    token-major layout), then one scale per block of 64 tokens of each head,
+    2^u / 112 with u uniform in [-1/2, 1/2] (so the dequantized values are
+    N(0, 1) up to a factor 2^(+-1/2) per block).  Draw order: Q, K, V codes,
+    then the Q, K, V scales.  Dense only."""
+    if isinstance(spec, str):
+        spec = FP8_WORKLOADS[spec]
+    spec = dict(spec)
+    seed = spec.get("seed", 0) if seed is None else seed
+    rng = np.random.default_rng(seed)
+    B, hq, hkv, d = spec["B"], spec["Hq"], spec["Hkv"], spec["d"]
+    nq = spec.get("Nq", spec.get("N"))
+    nk = spec.get("Nk", spec.get("N"))
+    out = dict(spec, Nq=nq, Nk=nk)
+
+    def codes(shape):
+        x = np.empty(shape, np.float32)
+        flat = x.reshape(-1)
+        step = 1 << 24
+        for s in range(0, flat.size, step):
+            n = min(step, flat.size - s)
+            flat[s:s + n] = np.clip(rng.standard_normal(n, dtype=np.float32) * 112.0,
+                                    -448.0, 448.0)
+        return e4m3_codes(x)
+
+    out["q8"] = codes((B, nq, hq, d))
+    out["k8"] = codes((B, nk, hkv, d))
+    out["v8"] = codes((B, nk, hkv, d))
+    scl = lambda h, n: (2.0 ** rng.uniform(-0.5, 0.5, size=(B, h, -(-n // 64))) / 112.0
+                        ).astype(np.float32)
+    out["sq"], out["sk"], out["sv"] = scl(hq, nq), scl(hkv, nk), scl(hkv, nk)
+    out["scale"] = spec.get("scale", 1.0 / math.sqrt(d))
+    out.setdefault("causal", False)
+    out.setdefault("window", 0)
+    out["dtype"] = "fp8"
+    return out
+
+
+def transpose_v8(v8):
+    """Token-major V codes [B, N, H, d] -> the V^T layout [B, H, d, ldn]
+    (ldn = N rounded up to 64, zero padding) that the FP8 forward reads."""
+    B, N, H, d = v8.shape
+    ldn = -(-N // 64) * 64
+    out = np.zeros((B, H, d, ldn), dtype=np.uint8)
+    out[..., :N] = np.transpose(v8, (0, 2, 3, 1))
     return out
