@@ -23,6 +23,7 @@ Functions mirror the C ABI in include/fa_mi355x.h:
     fa_status_string(status) -> str
 """
 
+import contextlib
 import ctypes
 import math
 import os
@@ -43,63 +44,86 @@ class FaError(RuntimeError):
         super().__init__(f"{what}: {fa_status_string(status)} ({status})")
 
 
+LIB_DEBUG_SYNC_PATH = os.path.join(_HERE, "libfa_mi355x_debugsync.so")
+_override = None
+
+
 def lib():
     """The loaded ctypes library (raises if it has not been built)."""
     global _lib
+    if _override is not None:
+        return _override
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with "
-                "`python -m exact_io_aware_28_amd.build` (no fallback exists)")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-        fwd_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, vp]
-        L.fa_fwd.argtypes = fwd_args
-        L.fa_fwd.restype = i
-        L.fa_fwd_f16.argtypes = fwd_args
-        L.fa_fwd_f16.restype = i
-        L.fa_fwd_f32.argtypes = fwd_args
-        L.fa_fwd_f32.restype = i
-        L.fa_bwd_workspace_size.argtypes = [i, i, i]
-        L.fa_bwd_workspace_size.restype = ctypes.c_size_t
-        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                             i, i, i, i, i, i, f, i, i, vp, vp]
-        L.fa_bwd.restype = i
-        i64 = ctypes.c_int64
-        L.fa_fwd_bias.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
-                                  vp, i64, i64, i64, vp]
-        L.fa_fwd_bias.restype = i
-        L.fa_bwd_bias.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                  i, i, i, i, i, i, f, i, i, vp, i64, i64, i64, vp]
-        L.fa_bwd_bias.restype = i
-        u64 = ctypes.c_uint64
-        L.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, f,
-                                     u64, vp]
-        L.fa_fwd_dropout.restype = i
-        L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     ctypes.c_size_t, i, i, i, i, i, i, f, i, i, vp, f, u64,
-                                     vp]
-        L.fa_bwd_dropout.restype = i
-        L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
-        L.fa_decode_workspace_size.restype = ctypes.c_size_t
-        L.fa_decode_num_splits.argtypes = [i, i, i, i, i]
-        L.fa_decode_num_splits.restype = i
-        L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, vp,
-                                ctypes.c_size_t, vp]
-        L.fa_decode.restype = i
-        L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i,
-                                        vp]
-        L.fa_decode_noalloc.restype = i
-        L.fa_decode_noalloc_max_splits.argtypes = [i, i, i, i]
-        L.fa_decode_noalloc_max_splits.restype = i
-        L.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp]
-        L.fa_quantize_fp8.restype = i
-        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
-        L.fa_fwd_fp8.restype = i
-        L.fa_status_string.argtypes = [i]
-        L.fa_status_string.restype = ctypes.c_char_p
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Run the wrappers against another build of the same sources (the
+    stage-synchronised LIB_DEBUG_SYNC_PATH) inside the block."""
+    global _override
+    prev = _override
+    _override = _load(path)
+    try:
+        yield _override
+    finally:
+        _override = prev
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m exact_io_aware_28_amd.build --all` (no fallback exists)")
+    L = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fwd_args = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, vp]
+    L.fa_fwd.argtypes = fwd_args
+    L.fa_fwd.restype = i
+    L.fa_fwd_f16.argtypes = fwd_args
+    L.fa_fwd_f16.restype = i
+    L.fa_fwd_f32.argtypes = fwd_args
+    L.fa_fwd_f32.restype = i
+    L.fa_bwd_workspace_size.argtypes = [i, i, i]
+    L.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                         i, i, i, i, i, i, f, i, i, vp, vp]
+    L.fa_bwd.restype = i
+    i64 = ctypes.c_int64
+    L.fa_fwd_bias.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
+                              vp, i64, i64, i64, vp]
+    L.fa_fwd_bias.restype = i
+    L.fa_bwd_bias.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                              i, i, i, i, i, i, f, i, i, vp, i64, i64, i64, vp]
+    L.fa_bwd_bias.restype = i
+    u64 = ctypes.c_uint64
+    L.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, f,
+                                 u64, vp]
+    L.fa_fwd_dropout.restype = i
+    L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, i, i, i, i, i, i, f, i, i, vp, f, u64,
+                                 vp]
+    L.fa_bwd_dropout.restype = i
+    L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_decode_workspace_size.restype = ctypes.c_size_t
+    L.fa_decode_num_splits.argtypes = [i, i, i, i, i]
+    L.fa_decode_num_splits.restype = i
+    L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, vp,
+                            ctypes.c_size_t, vp]
+    L.fa_decode.restype = i
+    L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i,
+                                    vp]
+    L.fa_decode_noalloc.restype = i
+    L.fa_decode_noalloc_max_splits.argtypes = [i, i, i, i]
+    L.fa_decode_noalloc_max_splits.restype = i
+    L.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp]
+    L.fa_quantize_fp8.restype = i
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    L.fa_fwd_fp8.restype = i
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = ctypes.c_char_p
+    return L
 
 
 def fa_status_string(status):

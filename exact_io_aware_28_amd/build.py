@@ -1,9 +1,13 @@
 """Build libfa_mi355x.so for gfx950 in-tree with hipcc.
 
-    python -m exact_io_aware_28_amd.build [--jobs N] [--debug-sync]
+    python -m exact_io_aware_28_amd.build [--jobs N] [--debug-sync | --all]
 
 Each .hip source under csrc/ is compiled to an object in _build/ (in
-parallel), then linked into exact_io_aware_28_amd/libfa_mi355x.so.  Every
+parallel), then linked into exact_io_aware_28_amd/libfa_mi355x.so.  With
+--debug-sync the same sources are built with -DFA_DEBUG_SYNC (every staged
+copy completes and the work-group meets after each copy and each tile, so no
+copy overlaps a read of LDS) into libfa_mi355x_debugsync.so, whose results
+must equal the optimised library's bit for bit; --all builds both.  Every
 call recompiles everything.
 """
 
@@ -14,6 +18,7 @@ import subprocess
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_DEBUG_SYNC = os.path.join(PKG, "libfa_mi355x_debugsync.so")
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
@@ -43,8 +48,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src, extra, bdir):
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
            "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,26 +58,44 @@ def _compile(src, extra):
     return src, obj, r.returncode, msgs
 
 
-def build(jobs=None, extra=(), verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+VARIANTS = {  # name -> (extra compiler flags, object folder, library)
+    "release": ([], BUILD, LIB),
+    "debug_sync": (["-DFA_DEBUG_SYNC"], os.path.join(BUILD, "debug_sync"), LIB_DEBUG_SYNC),
+}
+
+
+def build(jobs=None, extra=(), verbose=False, variants=("release",)):
+    """Compile every source for each variant (one pool for all jobs), then
+    link each variant's library; returns the library paths."""
     srcs = sources()
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4)
-    objs = []
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        for src, obj, rc, msgs in ex.map(lambda s: _compile(s, list(extra)), srcs):
+    jobs = jobs or (os.cpu_count() or 4)
+    work = []
+    for v in variants:
+        flags, bdir, _ = VARIANTS[v]
+        os.makedirs(bdir, exist_ok=True)
+        work += [(v, src, list(extra) + flags, bdir) for src in srcs]
+    objs = {v: [] for v in variants}
+    with cf.ThreadPoolExecutor(min(jobs, len(work))) as ex:
+        futs = [(v, ex.submit(_compile, src, fl, bd)) for v, src, fl, bd in work]
+        for v, fut in futs:
+            src, obj, rc, msgs = fut.result()
             if msgs.strip() and (rc != 0 or verbose):
                 print(msgs, file=sys.stderr)
             if rc != 0:
-                raise RuntimeError(f"hipcc failed on {src}")
-            objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        print(r.stdout + r.stderr, file=sys.stderr)
-        raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
-    return LIB
+                raise RuntimeError(f"hipcc failed on {src} ({v})")
+            objs[v].append(obj)
+    libs = []
+    for v in variants:
+        lib = VARIANTS[v][2]
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs[v], "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            print(r.stdout + r.stderr, file=sys.stderr)
+            raise RuntimeError(f"link failed ({v})")
+        os.replace(tmp, lib)
+        libs.append(lib)
+    return libs[0] if len(libs) == 1 else libs
 
 
 def main(argv=None):
@@ -81,9 +104,15 @@ def main(argv=None):
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true",
                     help="print per-kernel register/LDS usage")
+    g = ap.add_mutually_exclusive_group()
+    g.add_argument("--debug-sync", action="store_true",
+                   help="build only libfa_mi355x_debugsync.so (-DFA_DEBUG_SYNC)")
+    g.add_argument("--all", action="store_true", help="build both libraries")
     a = ap.parse_args(argv)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if a.resource_usage else []
-    print(build(a.jobs, extra, a.verbose or a.resource_usage))
+    variants = (("release", "debug_sync") if a.all else
+                ("debug_sync",) if a.debug_sync else ("release",))
+    print(build(a.jobs, extra, a.verbose or a.resource_usage, variants))
 
 
 if __name__ == "__main__":

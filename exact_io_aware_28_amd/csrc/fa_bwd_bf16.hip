@@ -344,6 +344,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 
   // two buffers each, unrolled by two so that they are known at compile time
   if (n_it > 0) issue_it(0, sq0, sdo0);
+  FA_STAGE_SYNC();
   for (int it = 0; it < n_it; it += 2) {
     if (tid < kQTile) {
       sl0[tid] = lse_r;
@@ -351,7 +352,9 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
     }
     dma_barrier();  // tile it is in buffer 0; buffer 1 is free
     if (it + 1 < n_it) issue_it(it + 1, sq1, sdo1);
+    FA_STAGE_SYNC();
     compute(it, sq0, sdo0, sl0, sd0);
+    FA_STAGE_SYNC();
     if (it + 1 >= n_it) break;
     if (tid < kQTile) {
       sl1[tid] = lse_r;
@@ -359,7 +362,9 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
     }
     dma_barrier();  // tile it + 1 is in buffer 1; buffer 0 is free
     if (it + 2 < n_it) issue_it(it + 2, sq0, sdo0);
+    FA_STAGE_SYNC();
     compute(it + 1, sq1, sdo1, sl1, sd1);
+    FA_STAGE_SYNC();
   }
 
   if (kj < sp.lk) {
@@ -491,6 +496,7 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
     dma.issue(Vg, kstride_b, j0, sp.lk, vb);
   };
   if (kv_lo < kv_hi) issue(kv_lo, sk0, sv0);
+  FA_STAGE_SYNC();
 
   auto compute = [&](int j0, const __bf16* kt, const __bf16* vt) {
     bool active = qlo_w <= qhi_w;
@@ -590,11 +596,15 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   for (int j0 = kv_lo; j0 < kv_hi; j0 += 2 * kKTile) {
     dma_barrier();  // tile j0 is in buffer 0; buffer 1 is free
     if (j0 + kKTile < kv_hi) issue(j0 + kKTile, sk1, sv1);
+    FA_STAGE_SYNC();
     compute(j0, sk0, sv0);
+    FA_STAGE_SYNC();
     if (j0 + kKTile >= kv_hi) break;
     dma_barrier();  // tile j0 + kKTile is in buffer 1; buffer 0 is free
     if (j0 + 2 * kKTile < kv_hi) issue(j0 + 2 * kKTile, sk0, sv0);
+    FA_STAGE_SYNC();
     compute(j0 + kKTile, sk1, sv1);
+    FA_STAGE_SYNC();
   }
 
   if (qi < sp.lq) {

@@ -85,6 +85,7 @@ void decode_split_kernel(DecodeParams p) {
     dma.issue(Vg, kstride_b, s_lo + t * kDecBN, L, vb);
   };
   if (ntiles > 0) issue(0, k0, v0);
+  FA_STAGE_SYNC();
 
   // Q fragments (B operand of S^T = K Q^T): this lane's row, 8 columns per step
   bf16x8 qf[KS];
@@ -204,11 +205,15 @@ void decode_split_kernel(DecodeParams p) {
   for (int t = 0; t < ntiles; t += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t is in buffer 0
     if (t + 1 < ntiles) issue(t + 1, k1, v1);
+    FA_STAGE_SYNC();
     compute(s_lo + t * kDecBN, k0, v0);
+    FA_STAGE_SYNC();
     if (t + 1 >= ntiles) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t + 1 is in buffer 1
     if (t + 2 < ntiles) issue(t + 2, k0, v0);
+    FA_STAGE_SYNC();
     compute(s_lo + (t + 1) * kDecBN, k1, v1);
+    FA_STAGE_SYNC();
   }
 
   // normalised partial output and its logsumexp (an empty range: 0, -inf)

@@ -280,6 +280,23 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
+// Stage synchronisation for race hunting.  Built with -DFA_DEBUG_SYNC,
+// every staged copy completes (vmcnt 0) and the whole work-group meets after
+// each copy is issued and after each tile is computed, so no copy into LDS
+// overlaps any read of LDS; the optimised build must give the same bits.
+// Without the macro it is nothing.
+#ifdef FA_DEBUG_SYNC
+#define FA_STAGE_SYNC()                                \
+  do {                                                 \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   \
+    __syncthreads();                                   \
+  } while (0)
+#else
+#define FA_STAGE_SYNC() \
+  do {                  \
+  } while (0)
+#endif
+
 // ---------------------------------------------------------------- scheduling
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;

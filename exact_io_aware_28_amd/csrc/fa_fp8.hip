@@ -150,6 +150,7 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
     vdma.issue(Vg + j0, (uint32_t)p.ldv, D, vb);
   };
   if (kv_lo < kv_hi) issue(kv_lo, k0, v0);
+  FA_STAGE_SYNC();
 
   // ---- block scales of K and V for this (sequence, KV head); the largest V
   // scale of the visited tiles is the reference that keeps P <= 2^8.5
@@ -306,11 +307,15 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
   for (int j0 = kv_lo; j0 < kv_hi; j0 += 2 * kBN8) {
     dma_barrier();
     if (j0 + kBN8 < kv_hi) issue(j0 + kBN8, k1, v1);
+    FA_STAGE_SYNC();
     compute(j0, k0, v0);
+    FA_STAGE_SYNC();
     if (j0 + kBN8 >= kv_hi) break;
     dma_barrier();
     if (j0 + 2 * kBN8 < kv_hi) issue(j0 + 2 * kBN8, k0, v0);
+    FA_STAGE_SYNC();
     compute(j0 + kBN8, k1, v1);
+    FA_STAGE_SYNC();
   }
 
   // ---- epilogue: O = acc * sV_ref / l', LSE = ln 2 * (m + log2 l' - 7)

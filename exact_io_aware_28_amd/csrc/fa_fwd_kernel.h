@@ -127,6 +127,7 @@ void fwd_bf16_kernel(FwdParams p) {
     dma.issue(Vg, kstride_b, j0, sp.lk, vb);
   };
   if (kv_lo < kv_hi) issue(kv_lo, k0, v0);
+  FA_STAGE_SYNC();
 
   // ---- Q fragments (B operand of S^T = K Q^T): query qi, 8 columns per step
   const int qi = q_start + wave * 32 + r32;
@@ -320,11 +321,15 @@ void fwd_bf16_kernel(FwdParams p) {
   for (int j0 = kv_lo; j0 < kv_hi; j0 += 2 * kBN) {
     dma_barrier();  // tile j0 is in buffer 0; buffer 1 is free
     if (j0 + kBN < kv_hi) issue(j0 + kBN, k1, v1);
+    FA_STAGE_SYNC();
     compute(j0, k0, v0);
+    FA_STAGE_SYNC();
     if (j0 + kBN >= kv_hi) break;
     dma_barrier();  // tile j0 + kBN is in buffer 1; buffer 0 is free
     if (j0 + 2 * kBN < kv_hi) issue(j0 + 2 * kBN, k0, v0);
+    FA_STAGE_SYNC();
     compute(j0 + kBN, k1, v1);
+    FA_STAGE_SYNC();
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)

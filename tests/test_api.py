@@ -7,6 +7,7 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -313,3 +314,74 @@ def test_status_strings():
     for st in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
         assert fa.fa_status_string(st).startswith("FA_")
     assert "unknown" in fa.fa_status_string(99)
+
+
+# ------------------------------------------------- host AddressSanitizer run
+ASAN_RT = "/opt/rocm/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
+STUB_RUN = os.environ.get("FA_API_STUB_LAUNCHERS") == "1"
+
+
+@pytest.mark.skipif(not STUB_RUN, reason="only against the stub-launcher build (no GPU work)")
+def test_valid_calls_reach_the_launcher():
+    """With stub launchers every well-formed call passes its checks, fills its
+    parameter block and returns the launcher's failure as FA_ERR_HIP: the
+    whole host path of each entry point runs under the sanitizer."""
+    L = fa.lib()
+    for call in (lambda: _fwd(), lambda: _bwd(), lambda: _dec(), lambda: _fwd_bias(),
+                 lambda: _bwd_bias()):
+        assert call() == fa.FA_ERR_HIP
+    assert L.fa_quantize_fp8(P[0], P[1], P[2], 2, 100, 3, 128, 1, P[3], None) == fa.FA_ERR_HIP
+    assert L.fa_fwd_fp8(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 1, 4, 2, 100, 100, 128,
+                        0.1, 1, 0, None) == fa.FA_ERR_HIP
+
+
+def _host_build(tmp_path, srcs, out):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    cmd = [hipcc, "-x", "hip", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared", "-g",
+           "-O1", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address",
+           "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "exact_io_aware_28_amd", "csrc"), *srcs, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return out
+
+
+def _run_sanitized(script, lib):
+    env = dict(os.environ, LD_PRELOAD=ASAN_RT, FA_API_STUB_LAUNCHERS="1",
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:exitcode=86")
+    return subprocess.run([sys.executable, "-c", script, str(lib)], capture_output=True,
+                          text=True, env=env, cwd=ROOT, timeout=600)
+
+
+@pytest.mark.skipif(STUB_RUN or not os.path.exists(ASAN_RT), reason="needs the ASan runtime")
+def test_api_checks_under_address_sanitizer(tmp_path):
+    """The C ABI layer (csrc/fa_api.hip) built with host AddressSanitizer and
+    stub launchers; this file's checks run against it in a child process."""
+    lib = _host_build(tmp_path, [os.path.join(ROOT, "exact_io_aware_28_amd", "csrc",
+                                              "fa_api.hip"),
+                                 os.path.join(ROOT, "tests", "host", "api_stub_launchers.cpp")],
+                      tmp_path / "libfa_api_asan.so")
+    script = ("import sys, pytest\n"
+              "import exact_io_aware_28_amd as fa\n"
+              "fa.LIB_PATH = sys.argv[1]\n"
+              "sys.exit(pytest.main(['-q', '-p', 'no:cacheprovider', 'tests/test_api.py',\n"
+              "                      '-k', 'not sanitizer']))\n")
+    r = _run_sanitized(script, lib)
+    assert "AddressSanitizer" not in r.stderr, r.stderr[-3000:]
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-2000:]
+    summary = r.stdout.strip().splitlines()[-1]
+    assert " passed" in summary and "skipped" not in summary, summary
+
+
+@pytest.mark.skipif(STUB_RUN or not os.path.exists(ASAN_RT), reason="needs the ASan runtime")
+def test_sanitizer_harness_reports_a_heap_overflow(tmp_path):
+    """The same build and preload catch a real error: a host function that
+    reads one element past a heap buffer (test code, not the library)."""
+    src = tmp_path / "overflow.hip"
+    src.write_text('#include <cstdlib>\nextern "C" int past_the_end(int n) {\n'
+                   '  int* a = (int*)std::malloc(n * sizeof(int));\n'
+                   '  for (int i = 0; i < n; ++i) a[i] = i;\n'
+                   '  volatile int x = a[n];\n  std::free(a);\n  return x;\n}\n')
+    lib = _host_build(tmp_path, [str(src)], tmp_path / "liboverflow.so")
+    r = _run_sanitized("import ctypes, sys\nctypes.CDLL(sys.argv[1]).past_the_end(8)\n", lib)
+    assert r.returncode != 0 and "heap-buffer-overflow" in r.stderr, r.stderr[-2000:]

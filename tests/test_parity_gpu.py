@@ -339,3 +339,20 @@ def test_workload_long_fwd_bwd():
         check_grad(dq[b][qr][:, g:g + 1], rq, f"dQ b={b} h={g}")
         check_grad(dk[b, kr, g], rk, f"dK b={b} h={g}")
         check_grad(dv[b, kr, g], rv, f"dV b={b} h={g}")
+
+
+def test_workload_long_bwd_whole_head():
+    """Every element of dQ, dK and dV of one (batch, head) of the long
+    causal workload (B=2, H=16, N=16384, d=128), against the oracle's full
+    backward of that head (S, P and dP materialised in fp64, ~6.5 GB)."""
+    inp = workloads.make_inputs("long_fwd_bwd")
+    say("[bwd whole head] long_fwd_bwd B=2 H=16 N=16384 d=128 causal, head (b=1, h=9)")
+    dev = run_fwd(inp)
+    dq, dk, dv = run_bwd(inp, dev)
+    b, h = 1, 9
+    dq, dk, dv = (to_np(t[b:b + 1, :, h:h + 1]) for t in (dq, dk, dv))
+    one = lambda n: inp[n][b:b + 1, :, h:h + 1].astype(np.float64)
+    rq, rk, rv = oracle.attn_bwd(one("q"), one("k"), one("v"), one("do"), inp["scale"], True)
+    check_grad(dq, rq, "dQ whole head")
+    check_grad(dk, rk, "dK whole head")
+    check_grad(dv, rv, "dV whole head")
