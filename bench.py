@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--all] [--copy-calibration]
+    python bench.py --backward [--workload long_fwd_bwd] [--steps K] [--warmup W]
 
 One step = one fa_fwd call over the whole workload: work partition, Q/K/V
 tile loads, QK^T, masking, online softmax, PV and the epilogue all run in the
@@ -13,6 +14,10 @@ recorded on the stream the kernel runs on (torch's current stream).
 Prints one JSON line with the throughput in attention TFLOP/s (4 B Hq Nq Nk d,
 halved for causal), the roofline position of the forward kernel, and the CPU
 oracle timed on this host on a bounded sample of the same workload.
+With --backward it times only the backward call (D, dK/dV and dQ kernels) of
+a workload that has one and prints one line with its time and throughput on
+the five counted products (2.5x the forward count); this is the mode the
+backward's kernel traces and counters are taken from.
 """
 
 import argparse
@@ -342,6 +347,8 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true",
                     help="also time every other workload and the backward (extra lines)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time only the backward of --workload (default long_fwd_bwd)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -360,6 +367,19 @@ def main(argv=None):
 
     if a.copy_calibration:
         copy_calibration()
+        return 0
+
+    if a.backward:
+        name = a.workload if a.workload != "gqa_causal_prefill" else "long_fwd_bwd"
+        wi = workloads.make_inputs(name)
+        if not wi.get("bwd"):
+            print(f"bench.py: workload {name} has no backward", file=sys.stderr)
+            return 2
+        bms = time_backward(wi, device_inputs(wi), a.steps, a.warmup)
+        tf = 2.5 * attention_flops(wi) / (bms * 1e-3) / 1e12
+        print(json.dumps({"workload": name, "direction": "bwd", "steps": a.steps,
+                          "warmup": a.warmup, "ms": round(bms, 4), "TFLOP/s": round(tf, 2),
+                          "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
         return 0
 
     inp = workloads.make_inputs(a.workload)

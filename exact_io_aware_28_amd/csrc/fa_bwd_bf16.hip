@@ -15,11 +15,15 @@
 //
 // Three kernels, in stream order, no atomics (results are deterministic):
 //   1. bwd_pre:  D_i from dO and the saved bf16 O, into the workspace.
-//   2. bwd_dkdv: a work-group owns 128 keys of one KV head (one wave per 32
-//      keys, each lane one key); it walks every query head of the KV head's
-//      group and every query tile that can see its keys, with Q, dO, LSE and
-//      D tiles staged in LDS.  dK and dV stay in registers and are written
-//      once, so the GQA sum over the group needs no atomics.
+//   2. bwd_dkdv: a work-group owns 128 keys of one KV head (each lane one
+//      key); it walks every query head of the KV head's group and every
+//      query tile that can see its keys, with Q, dO, LSE and D tiles staged
+//      in LDS.  dK and dV stay in registers and are written once, so the GQA
+//      sum over the group needs no atomics.  For d = 128 (no dropout) eight
+//      waves share the work, K and V staged in LDS, each pair of waves
+//      splitting every query tile's rows and adding its partial sums at the
+//      end (bwd_dkdv8_kernel); otherwise four waves, one per 32 keys, with K
+//      and V in registers (bwd_dkdv_kernel).
 //   3. bwd_dq:   a work-group owns 128 query rows of one head (one lane per
 //      query row, as in the forward) and walks the key tiles it can see,
 //      rebuilding S and dP to accumulate dQ.  This recomputes two of the
@@ -388,6 +392,315 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
   }
 }
 
+// dK/dV with eight waves (two per SIMD) for d = 128.  The one-wave-per-SIMD
+// kernel above holds K and V in registers and waits on its own LDS reads and
+// products about 40 % of the time with nothing else to issue.  Here K and V
+// of the work-group's 128 keys sit in LDS instead (read as operand fragments
+// like Q and dO), which frees the 64 registers that let two waves share each
+// SIMD.  Waves w and w + 4 take the same 32 keys; wave w the first 32 rows of
+// every 64-row query tile, wave w + 4 the second 32, so each holds partial dK
+// and dV sums for its keys, and the pair adds them through LDS at the end
+// (the sum is over disjoint row sets, fixed by the launch shape, so results
+// stay deterministic).
+constexpr int kDkdv8Threads = 512;
+
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP>
+__global__ __launch_bounds__(kDkdv8Threads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr float kInf = __builtin_inff();
+  __shared__ __attribute__((aligned(1024))) __bf16 sk[kKeyBlock * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sv[kKeyBlock * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sq0[kQTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sdo0[kQTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sq1[kQTile * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sdo1[kQTile * D];
+  __shared__ __attribute__((aligned(16))) float sl0[kQTile], sd0[kQTile];
+  __shared__ __attribute__((aligned(16))) float sl1[kQTile], sd1[kQTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, r32 = lane & 31;
+  const int kw = wave & 3, hb = wave >> 2;  // 32-key block, query-row half
+
+  uint32_t id = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int kt = id % num_ktiles;
+  id /= num_ktiles;
+  const int b = id % p.B;
+  const int hkv = id / p.B;
+  const int G = p.group;
+  const int32_t* cu = VARLEN ? p.cu_seqlens : nullptr;
+  const SeqSpan sp = seq_span(cu, b, p.Nq, p.Nk);
+  const int k_start = kt * kKeyBlock;
+  if (k_start >= sp.lk) return;
+  const int delta = sp.lk - sp.lq;
+  const int k_end = min(k_start + kKeyBlock, sp.lk);
+
+  int q_lo = 0, q_hi = sp.lq;
+  if (CAUSAL) q_lo = max(0, k_start - delta);
+  if (WINDOW) q_hi = min(q_hi, p.window + k_end - 1 - delta);
+  q_lo = (q_lo / kQTile) * kQTile;
+  const int n_qt = (q_hi > q_lo) ? (q_hi - q_lo + kQTile - 1) / kQTile : 0;
+  const int n_it = n_qt * G;
+
+  const int64_t qstride = (int64_t)p.Hq * D, kstride = (int64_t)p.Hkv * D;
+  const float c = p.scale_log2;
+
+  const int kw_lo = k_start + kw * 32;
+  const int kw_hi = min(kw_lo + 31, sp.lk - 1);
+  const int kj = kw_lo + r32;
+
+  // K and V of the work-group's keys, staged once (rows past the sequence
+  // read as zero)
+  {
+    const uint32_t kstride_b = (uint32_t)(kstride * 2);
+    const TileDma<D, kKeyBlock, kDkdv8Threads / 64> kv(wave, lane, kstride_b);
+    const int64_t koff = sp.k0 * kstride + (int64_t)hkv * D;
+    kv.issue((const __bf16*)p.k + koff, kstride_b, k_start, sp.lk, sk);
+    kv.issue((const __bf16*)p.v + koff, kstride_b, k_start, sp.lk, sv);
+  }
+
+  f32x16 dva[DB], dka[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dva[db][i] = dka[db][i] = 0.f;
+
+  // Lane byte offsets of the LDS reads: 128-bit fragments of this wave's 32
+  // query rows (Q, dO) and of its 32 keys (K, V), and transposing reads of
+  // its query rows per output column block.  The swizzle depends on the row
+  // modulo 16 only, so the row-half and key-block offsets are whole rows.
+  const int tr_row = 4 * hl + ((lane & 15) >> 2);
+  const int tr_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  uint32_t fq[KS], fk[KS], troff[2][DB];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    const uint32_t f = 2 * tile_off<D>(r32, st * 16 + hl * 8);
+    fq[st] = f + (uint32_t)(hb * 32 * D * 2);
+    fk[st] = f + (uint32_t)(kw * 32 * D * 2);
+  }
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      troff[h2][db] = 2 * tile_off<D>(tr_row + 8 * h2, db * 32 + tr_col) +
+                      (uint32_t)(hb * 32 * D * 2);
+
+  const uint32_t qstride_b = (uint32_t)(qstride * 2);
+  const TileDma<D, kQTile, kDkdv8Threads / 64> dma(wave, lane, qstride_b);
+  float lse_r = 0.f, dl_r = 0.f;  // row statistics of the next tile (threads < kQTile)
+  auto issue_it = [&](int it, __bf16* bq, __bf16* bdo) {
+    const int gi = it / n_qt;
+    const int i0 = q_lo + (it % n_qt) * kQTile;
+    const int h = hkv * G + gi;
+    const int64_t hoff = sp.q0 * qstride + (int64_t)h * D;
+    dma.issue((const __bf16*)p.q + hoff, qstride_b, i0, sp.lq, bq);
+    dma.issue((const __bf16*)p.dout + hoff, qstride_b, i0, sp.lq, bdo);
+    if (tid < kQTile) {
+      const int i = i0 + tid;
+      float l = kInf, dd = 0.f;
+      if (i < sp.lq) {
+        const int64_t li = lse_index(cu, p.B, p.Hq, p.Nq, b, h, sp.q0, i);
+        const float lv = p.lse[li];
+        l = (lv == -kInf) ? kInf : lv * kLog2e;  // rows that see no key: P = 0
+        dd = p.delta[li];
+      }
+      lse_r = l;
+      dl_r = dd;
+    }
+  };
+
+  auto compute = [&](int it, const __bf16* tq, const __bf16* tdo, const float* tl,
+                     const float* td) {
+    const int i0 = q_lo + (it % n_qt) * kQTile;
+    const int h_it = hkv * G + it / n_qt;  // query head of this tile
+    const int qr0 = i0 + hb * 32;
+    const int qr1 = min(qr0 + 31, sp.lq - 1);
+    bool active = (qr0 <= qr1) && (kw_lo <= kw_hi);
+    if (CAUSAL) active = active && (qr1 + delta >= kw_lo);
+    if (WINDOW) active = active && (qr0 + delta - kw_hi < p.window);
+    if (!active) return;
+    bool need_mask = false;
+    if (CAUSAL) need_mask = need_mask || (qr0 + delta < kw_hi);
+    if (WINDOW) need_mask = need_mask || (qr1 + delta - kw_lo >= p.window);
+
+    // bias at this lane's key for the block's 16 query rows, log2 units
+    float bv[BIAS ? 16 : 1];
+    if constexpr (BIAS) {
+      const float* bcol = p.bias + (int64_t)b * p.bias_sb + (int64_t)h_it * p.bias_sh +
+                          min(kj, sp.lk - 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qr = qr0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+        bv[i] = (kj < sp.lk && qr < sp.lq) ? bcol[(int64_t)qr * p.bias_sq] * kLog2e : 0.f;
+      }
+    }
+
+    // S = Q K^T and dP = dO V^T: lane = key kj, rows = queries
+    // hb*32 + 8(i/4) + 4hl + i%4 of the staged tile
+    f32x16 s, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      s = mfma32(as_bf16x8(lds_read_b128_at(tq, fq[st], 0)),
+                 as_bf16x8(lds_read_b128_at(sk, fk[st], 0)), s);
+      dp = mfma32(as_bf16x8(lds_read_b128_at(tdo, fq[st], 0)),
+                  as_bf16x8(lds_read_b128_at(sv, fk[st], 0)), dp);
+    }
+
+    // dropout keep bits, drawn and shared as in the one-wave-per-SIMD kernel
+    uint32_t kwd[8];
+    if constexpr (DROP) {
+      const int t = r32 & 3, a = (r32 >> 3) & 1, u = 4 * a + t;
+      uint32_t mine = 0;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int rho = 2 * u + k2;
+        const int row = qr0 + 8 * (rho >> 2) + 4 * hl + (rho & 3);
+        mine |= keep8(kj, row, h_it, b, p.seed_lo, p.seed_hi, p.drop_thresh) << (8 * k2);
+      }
+      const uint32_t other = row_ror8(mine);
+      const uint32_t own_w[4] = {quad_bcast<0>(mine), quad_bcast<1>(mine),
+                                 quad_bcast<2>(mine), quad_bcast<3>(mine)};
+      const uint32_t oth_w[4] = {quad_bcast<0>(other), quad_bcast<1>(other),
+                                 quad_bcast<2>(other), quad_bcast<3>(other)};
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        kwd[v] = (((v >> 2) == a) ? own_w[v & 3] : oth_w[v & 3]) >> u;
+    }
+
+    auto grads = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qrow = hb * 32 + 8 * r + 4 * hl;
+        const float4 L = *reinterpret_cast<const float4*>(&tl[qrow]);
+        const float4 Dl = *reinterpret_cast<const float4*>(&td[qrow]);
+        const float Lv[4] = {L.x, L.y, L.z, L.w};
+        const float Dv[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r + e;
+          float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - Lv[e] : -Lv[e]));
+          if (MASKED)
+            pv = visible<CAUSAL, WINDOW>(i0 + qrow + e, kj, delta, sp.lk, p.window) ? pv : 0.f;
+          if constexpr (DROP) {
+            const bool kp = (kwd[i >> 1] >> (8 * (i & 1))) & 1u;
+            s[i] = kp ? pv * p.drop_scale : 0.f;
+            dp[i] = pv * ((kp ? dp[i] * p.drop_scale : 0.f) - Dv[e]);
+          } else {
+            s[i] = pv;
+            dp[i] = pv * (dp[i] - Dv[e]);
+          }
+        }
+      }
+    };
+    if (need_mask)
+      grads(std::true_type{});
+    else
+      grads(std::false_type{});
+
+    // dV^T += dO^T P and dK^T += Q^T dS over 16-query chunks; chunk qc
+    // holds queries 16qc + 4hl + {0..3} and 16qc + 8 + 4hl + {0..3} of the
+    // wave's row half
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      const int j = qc * 8;
+      const bf16x8 pb = pack_bf16x8(s[j], s[j + 1], s[j + 2], s[j + 3], s[j + 4],
+                                    s[j + 5], s[j + 6], s[j + 7]);
+      const bf16x8 dsb = pack_bf16x8(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
+                                     dp[j + 5], dp[j + 6], dp[j + 7]);
+      const uint32_t ro = 16 * qc * D * 2;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = mfma32(cat(lds_read_tr_at(tdo, troff[0][db], ro),
+                             lds_read_tr_at(tdo, troff[1][db], ro)),
+                         pb, dva[db]);
+        dka[db] = mfma32(cat(lds_read_tr_at(tq, troff[0][db], ro),
+                             lds_read_tr_at(tq, troff[1][db], ro)),
+                         dsb, dka[db]);
+      }
+    }
+  };
+
+  if (n_it > 0) issue_it(0, sq0, sdo0);
+  FA_STAGE_SYNC();
+  for (int it = 0; it < n_it; it += 2) {
+    if (tid < kQTile) {
+      sl0[tid] = lse_r;
+      sd0[tid] = dl_r;
+    }
+    dma_barrier();  // tile it (and, first, K and V) in place; buffer 1 is free
+    if (it + 1 < n_it) issue_it(it + 1, sq1, sdo1);
+    FA_STAGE_SYNC();
+    compute(it, sq0, sdo0, sl0, sd0);
+    FA_STAGE_SYNC();
+    if (it + 1 >= n_it) break;
+    if (tid < kQTile) {
+      sl1[tid] = lse_r;
+      sd1[tid] = dl_r;
+    }
+    dma_barrier();  // tile it + 1 is in buffer 1; buffer 0 is free
+    if (it + 2 < n_it) issue_it(it + 2, sq0, sdo0);
+    FA_STAGE_SYNC();
+    compute(it + 1, sq1, sdo1, sl1, sd1);
+    FA_STAGE_SYNC();
+  }
+
+  // Pair sum through LDS: the second row half hands over its dV partial, the
+  // first its dK partial (each 16 f32x4 per lane, stored so that every
+  // instruction writes 1 KB of consecutive bytes); then the first half
+  // finishes dV and the second dK.  With no tile at all the K/V copies are
+  // still in flight: wait for them before the buffers are reused.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x4* xv = reinterpret_cast<f32x4*>(kw < 2 ? sk : sv) + (kw & 1) * (DB * 4 * 64);
+  f32x4* xk = reinterpret_cast<f32x4*>(kw == 0 ? sq0 : kw == 1 ? sdo0 : kw == 2 ? sq1 : sdo1);
+  if (hb == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xv[(db * 4 + r) * 64 + lane] = f32x4{dva[db][4 * r], dva[db][4 * r + 1],
+                                             dva[db][4 * r + 2], dva[db][4 * r + 3]};
+  } else {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xk[(db * 4 + r) * 64 + lane] = f32x4{dka[db][4 * r], dka[db][4 * r + 1],
+                                             dka[db][4 * r + 2], dka[db][4 * r + 3]};
+  }
+  __syncthreads();
+  if (kj >= sp.lk) return;
+  const int64_t off = (sp.k0 + kj) * kstride + (int64_t)hkv * D;
+  if (hb == 0) {
+    __bf16* dvp = (__bf16*)p.dv + off;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 o = xv[(db * 4 + r) * 64 + lane];
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(dva[db][4 * r + e] + o[e]);
+        *reinterpret_cast<uint2*>(dvp + db * 32 + r * 8 + hl * 4) = __builtin_bit_cast(uint2, w);
+      }
+  } else {
+    __bf16* dkp = (__bf16*)p.dk + off;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 o = xk[(db * 4 + r) * 64 + lane];
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)((o[e] + dka[db][4 * r + e]) * p.scale);
+        *reinterpret_cast<uint2*>(dkp + db * 32 + r * 8 + hl * 4) = __builtin_bit_cast(uint2, w);
+      }
+  }
+}
+
 // ------------------------------------------------------------ 3. dQ
 // Two waves per SIMD; the unmasked and the biased d = 128 instances do not
 // fit their 256 registers without spilling and run one wave per SIMD instead.
@@ -621,12 +934,23 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   }
 }
 
+// dK/dV kernel choice: the eight-wave kernel for d = 128 without dropout.
+// d = 64 already runs two waves per SIMD in the four-wave kernel; with
+// dropout the eight-wave kernel spills 40-60 registers (the keep-bit words)
+// and measured 3.36 vs 2.61 ms on the dropout workload.
+template <int D, bool DROP>
+constexpr bool kUseDkdv8 = D == 128 && !DROP;
+
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false, bool DROP = false>
 hipError_t launch4(const BwdParams& p, hipStream_t stream) {
   const int nkt = (p.Nk + kKeyBlock - 1) / kKeyBlock;
   const int nqt = (p.Nq + kQBlock - 1) / kQBlock;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
-                     dim3((unsigned)p.B * p.Hkv * nkt), dim3(kThreads), 0, stream, p, nkt);
+  if constexpr (kUseDkdv8<D, DROP>)
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
+                       dim3((unsigned)p.B * p.Hkv * nkt), dim3(kDkdv8Threads), 0, stream, p, nkt);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
+                       dim3((unsigned)p.B * p.Hkv * nkt), dim3(kThreads), 0, stream, p, nkt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
