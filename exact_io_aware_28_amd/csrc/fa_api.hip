@@ -72,7 +72,6 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
   p.num_qtiles = 0;  // set by the launcher from its tile height
   p.bias = nullptr;
   p.bias_sb = p.bias_sh = p.bias_sq = 0;
-  p.bias_vec4 = 0;
   p.dropout = 0;
   p.drop_thresh = 0;
   p.seed_lo = p.seed_hi = 0;
@@ -91,11 +90,13 @@ int check_dropout(float dropout_p, uint32_t* thresh, float* scale) {
 }
 
 // An additive bias: non-null, 4-byte aligned, non-negative element strides.
-// Rows are read with 128-bit loads when every row start is 16-byte aligned.
-int check_bias(const float* bias, int64_t sb, int64_t sh, int64_t sq, int* vec4) {
+// The kernels read a wave's 32 bias rows through one buffer descriptor whose
+// byte range, at most (31 sq + Nk) x 4, must stay below 2^32.
+int check_bias(const float* bias, int64_t sb, int64_t sh, int64_t sq, int Nk) {
   if (!bias || !aligned(bias, 4)) return FA_ERR_INVALID_ARG;
   if (sb < 0 || sh < 0 || sq < 0) return FA_ERR_INVALID_ARG;
-  *vec4 = aligned(bias, 16) && sb % 4 == 0 && sh % 4 == 0 && sq % 4 == 0;
+  if (sq > ((int64_t)1 << 40) || (31 * sq + (int64_t)Nk) * 4 >= ((int64_t)1 << 32))
+    return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -159,8 +160,7 @@ int fa_fwd_bias(const void* q, const void* k, const void* v, void* o, float* lse
   int st = check_common(t, 4, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window, nullptr,
                         64);
   if (st != FA_OK) return st;
-  int vec4 = 0;
-  st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_q, &vec4);
+  st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_q, Nk);
   if (st != FA_OK) return st;
   fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
                                window, nullptr);
@@ -168,7 +168,6 @@ int fa_fwd_bias(const void* q, const void* k, const void* v, void* o, float* lse
   p.bias_sb = bias_stride_b;
   p.bias_sh = bias_stride_h;
   p.bias_sq = bias_stride_q;
-  p.bias_vec4 = vec4;
   return fa::launch_fwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -184,9 +183,8 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o,
   int st = check_common(t, 9, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
                         cu_seqlens, 64);
   if (st != FA_OK) return st;
-  int vec4 = 0;
   if (has_bias) {
-    st = check_bias(bias, sb, sh, sq, &vec4);
+    st = check_bias(bias, sb, sh, sq, Nk);
     if (st != FA_OK) return st;
   }
   uint32_t thresh = 0;
@@ -205,7 +203,6 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o,
   p.bias_sb = sb;
   p.bias_sh = sh;
   p.bias_sq = sq;
-  p.bias_vec4 = vec4;
   p.q = q;
   p.k = k;
   p.v = v;

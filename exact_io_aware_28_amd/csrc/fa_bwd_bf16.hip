@@ -149,6 +149,11 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
   q_lo = (q_lo / kQTile) * kQTile;
   const int n_qt = (q_hi > q_lo) ? (q_hi - q_lo + kQTile - 1) / kQTile : 0;
   const int n_it = n_qt * G;
+  // iteration it -> (query head of the group, query tile).  With a bias the
+  // head is the fastest index: the G heads that share a bias block (a bias
+  // broadcast over heads) then read it back to back, from the caches.
+  auto it_head = [&](int it) { return BIAS ? it % G : it / n_qt; };
+  auto it_tile = [&](int it) { return BIAS ? it / G : it % n_qt; };
 
   const int64_t qstride = (int64_t)p.Hq * D, kstride = (int64_t)p.Hkv * D;
   const float c = p.scale_log2;
@@ -199,8 +204,8 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
   const TileDma<D, kQTile, kThreads / 64> dma(wave, lane, qstride_b);
   float lse_r = 0.f, dl_r = 0.f;  // row statistics of the next tile (threads < kQTile)
   auto issue_it = [&](int it, __bf16* bq, __bf16* bdo) {
-    const int gi = it / n_qt;
-    const int i0 = q_lo + (it % n_qt) * kQTile;
+    const int gi = it_head(it);
+    const int i0 = q_lo + it_tile(it) * kQTile;
     const int h = hkv * G + gi;
     const int64_t hoff = sp.q0 * qstride + (int64_t)h * D;
     dma.issue((const __bf16*)p.q + hoff, qstride_b, i0, sp.lq, bq);
@@ -221,8 +226,8 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 
   auto compute = [&](int it, const __bf16* tq, const __bf16* tdo, const float* tl,
                      const float* td) {
-    const int i0 = q_lo + (it % n_qt) * kQTile;
-    const int h_it = hkv * G + it / n_qt;  // query head of this tile
+    const int i0 = q_lo + it_tile(it) * kQTile;
+    const int h_it = hkv * G + it_head(it);  // query head of this tile
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qr0 = i0 + qb * 32;
@@ -236,16 +241,17 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
       if (WINDOW) need_mask = need_mask || (qr1 + delta - kw_lo >= p.window);
 
       // bias at this lane's key for the block's 16 query rows (a column of
-      // the bias: consecutive lanes read consecutive keys), log2 units
+      // the bias: consecutive lanes read consecutive keys), raw values that
+      // are scaled to log2 units where they are used
       float bv[BIAS ? 16 : 1];
       if constexpr (BIAS) {
-        const int hb = hkv * G + it / n_qt;
+        const int hb = hkv * G + it_head(it);
         const float* bcol = p.bias + (int64_t)b * p.bias_sb + (int64_t)hb * p.bias_sh +
                             min(kj, sp.lk - 1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qr = qr0 + 8 * (i >> 2) + 4 * hl + (i & 3);
-          bv[i] = (kj < sp.lk && qr < sp.lq) ? bcol[(int64_t)qr * p.bias_sq] * kLog2e : 0.f;
+          bv[i] = (kj < sp.lk && qr < sp.lq) ? bcol[(int64_t)qr * p.bias_sq] : 0.f;
         }
       }
 
@@ -301,7 +307,9 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * r + e;
-            float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - Lv[e] : -Lv[e]));
+            float pv = fmaf(s[i], c, -Lv[e]);
+            if constexpr (BIAS) pv = fmaf(bv[i], kLog2e, pv);
+            pv = fast_exp2(pv);
             if (MASKED)
               pv = visible<CAUSAL, WINDOW>(i0 + qrow + e, kj, delta, sp.lk, p.window) ? pv : 0.f;
             if constexpr (DROP) {
@@ -441,6 +449,11 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
   q_lo = (q_lo / kQTile) * kQTile;
   const int n_qt = (q_hi > q_lo) ? (q_hi - q_lo + kQTile - 1) / kQTile : 0;
   const int n_it = n_qt * G;
+  // iteration it -> (query head of the group, query tile).  With a bias the
+  // head is the fastest index: the G heads that share a bias block (a bias
+  // broadcast over heads) then read it back to back, from the caches.
+  auto it_head = [&](int it) { return BIAS ? it % G : it / n_qt; };
+  auto it_tile = [&](int it) { return BIAS ? it / G : it % n_qt; };
 
   const int64_t qstride = (int64_t)p.Hq * D, kstride = (int64_t)p.Hkv * D;
   const float c = p.scale_log2;
@@ -489,8 +502,8 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
   const TileDma<D, kQTile, kDkdv8Threads / 64> dma(wave, lane, qstride_b);
   float lse_r = 0.f, dl_r = 0.f;  // row statistics of the next tile (threads < kQTile)
   auto issue_it = [&](int it, __bf16* bq, __bf16* bdo) {
-    const int gi = it / n_qt;
-    const int i0 = q_lo + (it % n_qt) * kQTile;
+    const int gi = it_head(it);
+    const int i0 = q_lo + it_tile(it) * kQTile;
     const int h = hkv * G + gi;
     const int64_t hoff = sp.q0 * qstride + (int64_t)h * D;
     dma.issue((const __bf16*)p.q + hoff, qstride_b, i0, sp.lq, bq);
@@ -511,8 +524,8 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 
   auto compute = [&](int it, const __bf16* tq, const __bf16* tdo, const float* tl,
                      const float* td) {
-    const int i0 = q_lo + (it % n_qt) * kQTile;
-    const int h_it = hkv * G + it / n_qt;  // query head of this tile
+    const int i0 = q_lo + it_tile(it) * kQTile;
+    const int h_it = hkv * G + it_head(it);  // query head of this tile
     const int qr0 = i0 + hb * 32;
     const int qr1 = min(qr0 + 31, sp.lq - 1);
     bool active = (qr0 <= qr1) && (kw_lo <= kw_hi);
@@ -523,7 +536,8 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
     if (CAUSAL) need_mask = need_mask || (qr0 + delta < kw_hi);
     if (WINDOW) need_mask = need_mask || (qr1 + delta - kw_lo >= p.window);
 
-    // bias at this lane's key for the block's 16 query rows, log2 units
+    // bias at this lane's key for the block's 16 query rows (raw values,
+    // scaled to log2 units where they are used)
     float bv[BIAS ? 16 : 1];
     if constexpr (BIAS) {
       const float* bcol = p.bias + (int64_t)b * p.bias_sb + (int64_t)h_it * p.bias_sh +
@@ -531,7 +545,7 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qr = qr0 + 8 * (i >> 2) + 4 * hl + (i & 3);
-        bv[i] = (kj < sp.lk && qr < sp.lq) ? bcol[(int64_t)qr * p.bias_sq] * kLog2e : 0.f;
+        bv[i] = (kj < sp.lk && qr < sp.lq) ? bcol[(int64_t)qr * p.bias_sq] : 0.f;
       }
     }
 
@@ -581,7 +595,9 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
-          float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - Lv[e] : -Lv[e]));
+          float pv = fmaf(s[i], c, -Lv[e]);
+          if constexpr (BIAS) pv = fmaf(bv[i], kLog2e, pv);
+          pv = fast_exp2(pv);
           if (MASKED)
             pv = visible<CAUSAL, WINDOW>(i0 + qrow + e, kj, delta, sp.lk, p.window) ? pv : 0.f;
           if constexpr (DROP) {
@@ -779,10 +795,9 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 
   const int qlo_w = q_start + wave * 32;
   const int qhi_w = min(qlo_w + 31, sp.lq - 1);
-  const float* brow = nullptr;  // this lane's bias row
-  if constexpr (BIAS)
-    brow = p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
-           (int64_t)min(qi, sp.lq - 1) * p.bias_sq;
+  const float* bias_bh = BIAS ? p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh
+                              : nullptr;
+  const uint32_t bias_lane = (uint32_t)(r32 * p.bias_sq) * 4u;
 
   // Lane byte offsets of the LDS reads inside a K or V tile (same swizzled
   // layout as the forward): 128-bit fragment reads per k-step, transposing
@@ -828,10 +843,13 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       // bias of this lane's row at keys j0 + 32kb + 8g + 4hl + {0..3}
       float bv[BIAS ? 16 : 1];
       if constexpr (BIAS) {
+        const __amdgpu_buffer_rsrc_t rs = bias_rsrc(bias_bh, p.bias_sq, qlo_w, sp.lq, j0, sp.lk);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          bias4(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq, p.bias_vec4 != 0,
-                kLog2e, &bv[4 * g]);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 t = bias_load4(rs, bias_lane, kb * 32 + g * 8 + hl * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bv[4 * g + e] = t[e];
+        }
       }
       f32x16 s, dp;
 #pragma unroll
@@ -865,7 +883,9 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(s[i], c, BIAS ? bv[i] - lse2 : -lse2));
+        float pv = fmaf(s[i], c, -lse2);
+        if constexpr (BIAS) pv = fmaf(bv[i], kLog2e, pv);
+        pv = fast_exp2(pv);
         if (MASKED) {
           const int off = (i >> 2) * 8 + (i & 3);
           bool ok = off < end;

@@ -88,24 +88,6 @@ __device__ __forceinline__ uint2 pack4_t(float a0, float a1, float a2, float a3)
   }
 }
 
-// Four consecutive entries row[j .. j+3] of an additive-bias row, times
-// `mult` (log2(e): the kernels work in log2 units).  Entries at or past `lim` and rows that
-// do not exist (row_ok false) read as 0 without touching memory; `vec`: the
-// row start is 16-byte aligned, so j % 4 == 0 allows one 128-bit load.
-__device__ __forceinline__ void bias4(const float* row, int j, int lim, bool row_ok, bool vec,
-                                      float mult, float* out) {
-  if (row_ok && vec && j + 4 <= lim) {
-    const float4 t = *reinterpret_cast<const float4*>(row + j);
-    out[0] = t.x * mult;
-    out[1] = t.y * mult;
-    out[2] = t.z * mult;
-    out[3] = t.w * mult;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = (row_ok && j + e < lim) ? row[j + e] * mult : 0.f;
-  }
-}
-
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }
@@ -270,6 +252,26 @@ struct TileDma {
     for (int i = 0; i < kPerWave; ++i) dma16(r, lds + (first + i) * 512, voff[i]);
   }
 };
+
+// Additive-bias block of one wave: its 32 rows r0 .. r0 + 31 (lane row r32)
+// from column j0 on, read four consecutive fp32 entries per load.  One
+// buffer descriptor spans the block up to the last valid element (row lq - 1,
+// column lk - 1), so a load in a row past the sequence, or past its last key
+// in that last row, returns 0 with no branch; in the other rows, keys past
+// the end read the next row's entries, which the key mask discards.  The
+// byte range is at most (31 sq + lk) x 4, which the C API bounds below 2^32.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bias_rsrc(const float* bias_bh, int64_t sq,
+                                                            int r0, int lq, int j0, int lk) {
+  const int rows = min(lq - r0, 32);
+  const uint32_t nbytes = rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * sq + (lk - j0)) * 4) : 0u;
+  return make_rsrc(bias_bh + (int64_t)r0 * sq + j0, nbytes);
+}
+// Entries (row r0 + r32, columns j0 + col .. + 3); lane_off = (r32 sq) x 4.
+__device__ __forceinline__ f32x4 bias_load4(__amdgpu_buffer_rsrc_t rs, uint32_t lane_off,
+                                            int col) {
+  return __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(lane_off + (uint32_t)col * 4u), 0, 0));
+}
 
 // Barrier that publishes LDS-DMA data to the whole work-group: every wave
 // first waits for its own outstanding buffer->LDS loads (vmcnt 0), then all

@@ -94,13 +94,24 @@ void fwd_bf16_kernel(FwdParams p) {
   const int G = p.group;
   const int gi = id % G;
   id /= G;
-  const int t_ord = id % p.num_qtiles;
-  id /= p.num_qtiles;
-  // the KV head is the slowest index, so each XCD's contiguous range holds
-  // whole KV heads (their query heads share the K/V in that XCD's L2) and
-  // every XCD sees the same mix of sequences (balanced for packed batches)
-  const int b = id % p.B;
-  const int hkv = id / p.B;
+  int t_ord, b, hkv;
+  if (BIAS && p.bias_sh == 0) {
+    // a bias shared by the heads: every head of a query tile next to each
+    // other, so the work-groups that read the same bias rows run together
+    // on one XCD and share them in its L2
+    hkv = id % p.Hkv;
+    id /= p.Hkv;
+    t_ord = id % p.num_qtiles;
+    b = id / p.num_qtiles;
+  } else {
+    t_ord = id % p.num_qtiles;
+    id /= p.num_qtiles;
+    // the KV head is the slowest index, so each XCD's contiguous range holds
+    // whole KV heads (their query heads share the K/V in that XCD's L2) and
+    // every XCD sees the same mix of sequences (balanced for packed batches)
+    b = id % p.B;
+    hkv = id / p.B;
+  }
   const int h = hkv * G + gi;
   // causal: longest rows first so that the tail of the grid is short
   const int qt = CAUSAL ? (p.num_qtiles - 1 - t_ord) : t_ord;
@@ -154,10 +165,6 @@ void fwd_bf16_kernel(FwdParams p) {
   // with a bias the scores are turned into log2 units right after the
   // product, and the softmax update below multiplies by 1
   const float cs = BIAS ? 1.0f : c;
-  const float* brow = nullptr;  // this lane's bias row
-  if constexpr (BIAS)
-    brow = p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
-           (int64_t)min(qi, sp.lq - 1) * p.bias_sq;
 
   const int qlo_w = q_start + wave * 32;
   const int qhi_w = min(qlo_w + 31, sp.lq - 1);
@@ -178,6 +185,26 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db)
       voff[h][db] = 2 * tile_off<D>(tr_row + 8 * h, db * 32 + tr_col);
 
+  // The bias of this lane's row at the keys its score elements hold, for a
+  // whole tile (branch-free loads, bias_rsrc).
+  constexpr int kBiasRegs = BIAS ? NB * 16 : 1;
+  const uint32_t bias_lane = (uint32_t)(r32 * p.bias_sq) * 4u;
+  auto load_bias = [&](int j0, float (&bt)[kBiasRegs]) {
+    if constexpr (BIAS) {
+      const __amdgpu_buffer_rsrc_t rs =
+          bias_rsrc(p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh, p.bias_sq, qlo_w,
+                    sp.lq, j0, sp.lk);
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 t = bias_load4(rs, bias_lane, kb * 32 + g * 8 + hl * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bt[kb * 16 + 4 * g + e] = t[e];
+        }
+    }
+  };
+
   auto compute = [&](int j0, const __bf16* kt, const __bf16* vt) {
     bool active = qlo_w <= qhi_w;
     if (CAUSAL) active = active && (j0 <= qhi_w + delta);
@@ -187,6 +214,13 @@ void fwd_bf16_kernel(FwdParams p) {
     if (CAUSAL) need_mask = need_mask || (j0 + kBN - 1 > qlo_w + delta);
     if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
 
+    // the bias loads go out before the products, which hide part of their
+    // latency
+    float bt[kBiasRegs];
+    if constexpr (BIAS) {
+      load_bias(j0, bt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // S^T block kb: rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4, col = qi
     f32x16 s[NB];
 #pragma unroll
@@ -213,19 +247,11 @@ void fwd_bf16_kernel(FwdParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
     if constexpr (BIAS) {
-      // bias of this lane's row at the keys its score elements hold; the
-      // fence keeps the loads (and their registers) after the products
-      __builtin_amdgcn_sched_barrier(0);
+      // scores and bias in log2 units
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float bv[4];
-          bias4(brow, j0 + kb * 32 + g * 8 + hl * 4, sp.lk, qi < sp.lq, p.bias_vec4 != 0,
-                kLog2e, bv);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[kb][4 * g + e] = fmaf(s[kb][4 * g + e], c, bv[e]);
-        }
+        for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(bt[kb * 16 + i], kLog2e, s[kb][i] * c);
     }
 
     // Online-softmax update and P V product.  MASKED tiles straddle a mask

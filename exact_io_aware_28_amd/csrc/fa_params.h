@@ -27,7 +27,6 @@ struct FwdParams {
   // (b, h, i, j) at bias[b*bias_sb + h*bias_sh + i*bias_sq + j]
   const float* bias;
   int64_t bias_sb, bias_sh, bias_sq;
-  int bias_vec4;              // every row start is 16-byte aligned
   // dropout on the probabilities: element (b, h, i, j) is kept iff its 16-bit
   // slot of Philox4x32-10 (drop_call in fa_device.h), key (seed_lo,
   // seed_hi), is >= drop_thresh; kept values are multiplied by drop_scale
@@ -56,7 +55,6 @@ struct BwdParams {
   float scale_log2;
   const float* bias;          // as in FwdParams
   int64_t bias_sb, bias_sh, bias_sq;
-  int bias_vec4;
   int dropout;                // as in FwdParams
   uint32_t drop_thresh;
   uint32_t seed_lo, seed_hi;

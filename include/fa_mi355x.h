@@ -171,9 +171,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *          or a key-padding row with bias_stride_q = 0).
  *   bias_stride_* : element strides, >= 0
  * Returns FA_ERR_INVALID_ARG, in addition to fa_fwd's cases, for a NULL or
- * not 4-byte-aligned bias or a negative stride.  Rows are read 16 bytes at a
- * time when the bias is 16-byte aligned and every stride is a multiple of 4,
- * element by element otherwise (slower).  Entries must be finite or -inf.
+ * not 4-byte-aligned bias or a negative stride, and FA_ERR_UNSUPPORTED when
+ * (31 * bias_stride_q + Nk) * 4 >= 2^32 (the kernels address 32 bias rows
+ * of one head through one 32-bit byte range).  Entries must be finite or
+ * -inf.
  */
 int fa_fwd_bias(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int Hq, int Hkv, int Nq, int Nk, int d,

@@ -253,6 +253,8 @@ BAD_BIAS = [
     (dict(sb=-4), fa.FA_ERR_INVALID_ARG),
     (dict(sh=-1), fa.FA_ERR_INVALID_ARG),
     (dict(sq=-64), fa.FA_ERR_INVALID_ARG),
+    # 32 rows of one head must span less than 2^32 bytes: (31 sq + Nk) * 4
+    (dict(sq=(1 << 30) // 31), fa.FA_ERR_UNSUPPORTED),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
     (dict(causal=5), fa.FA_ERR_INVALID_ARG),
