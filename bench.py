@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--all] [--copy-calibration]
     python bench.py --backward [--workload long_fwd_bwd] [--steps K] [--warmup W]
+    python bench.py --decode [--steps K] [--warmup W]
 
 One step = one fa_fwd call over the whole workload: work partition, Q/K/V
 tile loads, QK^T, masking, online softmax, PV and the epilogue all run in the
@@ -17,7 +18,8 @@ oracle timed on this host on a bounded sample of the same workload.
 With --backward it times only the backward call (D, dK/dV and dQ kernels) of
 a workload that has one and prints one line with its time and throughput on
 the five counted products (2.5x the forward count); this is the mode the
-backward's kernel traces and counters are taken from.
+backward's kernel traces and counters are taken from.  --decode does the
+same for the split-KV decode workload (split and combine kernels).
 """
 
 import argparse
@@ -282,6 +284,16 @@ def time_decode(inp, steps, warmup):
     return timed(launch, steps, torch.cuda.current_stream())[0], splits
 
 
+def decode_line(name, steps, warmup):
+    di = workloads.make_decode_inputs(name)
+    dms, splits = time_decode(di, steps, warmup)
+    gbs = decode_bytes(di) / (dms * 1e-3) / 1e9
+    tf = 4.0 * di["Hq"] * di["d"] * decode_pairs(di) / (dms * 1e-3) / 1e12
+    return {"workload": name, "direction": "decode", "ms": round(dms, 4), "GB/s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "TFLOP/s": round(tf, 2),
+            "num_splits": splits, "algorithmic_bytes": decode_bytes(di)}
+
+
 def time_fp8(name, steps, warmup):
     """FP8 forward over resident E4M3 codes and block scales, and the
     quantizer that makes them from bf16 (Q and K rotated, V transposed)."""
@@ -349,6 +361,8 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time only the backward of --workload (default long_fwd_bwd)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time only the split-KV decode workload")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -367,6 +381,11 @@ def main(argv=None):
 
     if a.copy_calibration:
         copy_calibration()
+        return 0
+
+    if a.decode:
+        for name in workloads.DECODE_WORKLOADS:
+            print(json.dumps(decode_line(name, a.steps, a.warmup)), flush=True)
         return 0
 
     if a.backward:
@@ -461,14 +480,7 @@ def main(argv=None):
             print(json.dumps(time_fp8(name, max(a.steps, 10), a.warmup)), flush=True)
             torch.cuda.empty_cache()
         for name in workloads.DECODE_WORKLOADS:
-            di = workloads.make_decode_inputs(name)
-            dms, splits = time_decode(di, max(a.steps, 10), a.warmup)
-            gbs = decode_bytes(di) / (dms * 1e-3) / 1e9
-            tf = 4.0 * di["Hq"] * di["d"] * decode_pairs(di) / (dms * 1e-3) / 1e12
-            print(json.dumps({"workload": name, "direction": "decode", "ms": round(dms, 4),
-                              "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                              "TFLOP/s": round(tf, 2), "num_splits": splits,
-                              "algorithmic_bytes": decode_bytes(di)}), flush=True)
+            print(json.dumps(decode_line(name, max(a.steps, 10), a.warmup)), flush=True)
             torch.cuda.empty_cache()
     return 0
 
