@@ -4,8 +4,9 @@ the fp64 oracle.
 The bias is fp32 and added to the scaled scores before the causal/window
 masks and the softmax; -inf entries hide keys.  Cases cover every broadcast
 the strides allow (per head, shared by the heads, a key-padding row shared by
-the query rows, a strided view), the 128-bit and the element-wise read paths
-(row strides that are and are not multiples of 4 floats), ragged tiles,
+the query rows, a strided view), 128-bit loads from rows that do and do not
+start on 16-byte boundaries (row strides that are and are not multiples of 4
+floats; the kernels clamp loads past the last valid entry), ragged tiles,
 chunked prefill (Nq < Nk), rows that the bias hides completely (O = 0,
 LSE = -inf, zero gradients), d = 64 and 128, MQA, and the full biased
 8192-token workload on sampled rows.  Tolerances as the unbiased path
