@@ -89,13 +89,80 @@ def check_lse(lse, ref, what=""):
     return mx
 
 
-def check_grad(g, ref, what=""):
+def check_grad(g, ref, what="", floor=None):
+    """Gradient bar: max |err| <= 5e-2 * max |ref|; with `floor` (an array
+    shaped like g, d_rounding_floor) each element may also differ by its
+    floor, the bound of the error that the bf16 O inside D carries."""
     scale = float(np.abs(ref).max())
-    mx = float(np.abs(g - ref).max())
-    say(f"  {what} max|err|={mx:.3e} max|ref|={scale:.3e} rel={mx / max(scale, 1e-30):.3e}")
+    err = np.abs(g - ref)
+    mx = float(err.max())
+    say(f"  {what} max|err|={mx:.3e} max|ref|={scale:.3e} rel={mx / max(scale, 1e-30):.3e}"
+        + ("" if floor is None else f" floor max={float(np.max(floor)):.3e}"))
     assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
-    assert mx <= GRAD_REL * scale, (what, mx, scale)
+    if floor is None:
+        assert mx <= GRAD_REL * scale, (what, mx, scale)
+    else:
+        excess = float((err - (GRAD_REL * scale + floor)).max())
+        assert excess <= 0.0, (what, mx, scale, excess)
     return mx / max(scale, 1e-30)
+
+
+def d_rounding_floor(inp, o, lse_ref):
+    """Elementwise first-order bound of the dQ and dK error that comes from
+    forming D_i = sum_c dO_ic O_ic from the bf16 O the backward receives (the
+    exact gradients use the exact O).  Rounding O to bf16 (to nearest) moves
+    D_i by at most e_i = 2^-9 sum_c |dO_ic O_ic|; through
+    dS_ij = P_ij (dP_ij - D_i) that moves dQ_ic by at most
+    scale e_i sum_j P_ij |K_jc|, and dK_jc by at most
+    scale sum_i P_ij e_i |Q_ic| (summed over the query heads of the KV head).
+    P (undropped, with the bias) is rebuilt from the oracle's LSE.  Matters
+    where the exact gradient vanishes, e.g. every row seeing one key with
+    dropout (D from the rounded O then differs from the kept dP).
+    Returns (floor_dq, floor_dk) shaped like Q and K."""
+    import oracle
+    q, k, do = (np.asarray(inp[n], np.float64) for n in ("q", "k", "do"))
+    o = np.asarray(o, np.float64)
+    scale, causal, window = inp["scale"], inp["causal"], inp["window"]
+    bias = inp.get("bias")
+    cu = inp.get("cu_seqlens")
+    if cu is None:
+        spans = [(b, None) for b in range(q.shape[0])]
+    else:
+        spans = [(None, (int(cu[s]), int(cu[s + 1]))) for s in range(len(cu) - 1)]
+    fq, fk = np.zeros_like(q), np.zeros_like(k)
+    hq, hkv = q.shape[-2], k.shape[-2]
+    g = hq // hkv
+    for b, span in spans:
+        if span is None:
+            qs, ks, dos, os_ = q[b], k[b], do[b], o[b]
+            lse = lambda h: np.asarray(lse_ref[b, h], np.float64)
+        else:
+            a, e = span
+            qs, ks, dos, os_ = q[a:e], k[a:e], do[a:e], o[a:e]
+            lse = lambda h, a=a, e=e: np.asarray(lse_ref[h, a:e], np.float64)
+        nq, nk = qs.shape[0], ks.shape[0]
+        if nq == 0 or nk == 0:
+            continue
+        ok = oracle.allowed_mask(nq, nk, causal, window)
+        for h in range(hq):
+            kv = h // g
+            s = scale * (qs[:, h] @ ks[:, kv].T)
+            if bias is not None:
+                s = s + np.broadcast_to(bias, (q.shape[0], hq, nq, nk))[b, h]
+            l = lse(h)
+            fin = np.isfinite(l)[:, None] & ok
+            with np.errstate(invalid="ignore", over="ignore"):  # rows that see no key
+                p = np.where(fin, np.exp(np.where(fin, s - l[:, None], -np.inf)), 0.0)
+            e_i = 2.0 ** -9 * np.abs(dos[:, h] * os_[:, h]).sum(axis=1)
+            fq_h = scale * e_i[:, None] * (p @ np.abs(ks[:, kv]))
+            fk_h = scale * (p * e_i[:, None]).T @ np.abs(qs[:, h])
+            if span is None:
+                fq[b, :, h] += fq_h
+                fk[b, :, kv] += fk_h
+            else:
+                fq[a:e, h] += fq_h
+                fk[a:e, kv] += fk_h
+    return fq, fk
 
 
 def sample_rows(n, tile=128, count=48, seed=0):
@@ -120,5 +187,5 @@ def is_close_bits(a, b):
 
 
 __all__ = ["say", "to_dev", "to_np", "run_fwd", "run_bwd", "check_o", "check_lse",
-           "dropout_bar_scale",
+           "dropout_bar_scale", "d_rounding_floor",
            "check_grad", "sample_rows", "math"]
