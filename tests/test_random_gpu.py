@@ -1,7 +1,7 @@
 """Seeded random sweep of the forward and backward against the fp64 oracle.
 
 The hand-picked cases elsewhere cover each feature on its own; this sweep
-draws 24 configurations that mix them: batch, query and key lengths not
+draws 40 configurations that mix them: batch, query and key lengths not
 tied to the tile sizes (chunked prefill and rows that see no key included),
 GQA group sizes 1-8, d = 64 and 128, causal and window masks, packed
 batches, and one of no bias, a bias (per head, shared by the heads, or a
@@ -23,7 +23,8 @@ from tests.gpu_util import (check_grad, check_lse, check_o, d_rounding_floor,
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 40
+N_DECODE = 16
 
 
 def _draw_cases(n=N_CASES, seed=20261203):
@@ -42,9 +43,9 @@ def _draw_cases(n=N_CASES, seed=20261203):
         if packed:
             case["lengths"] = [int(x) for x in rng.integers(0, 260, size=int(rng.integers(1, 5)))]
         else:
-            case["B"] = int(rng.integers(1, 3))
-            case["Nq"] = int(rng.integers(1, 330))
-            case["Nk"] = case["Nq"] if rng.random() < 0.6 else int(rng.integers(1, 330))
+            case["B"] = int(rng.integers(1, 4))
+            case["Nq"] = int(rng.integers(1, 520))
+            case["Nk"] = case["Nq"] if rng.random() < 0.6 else int(rng.integers(1, 520))
         if kind == "bias":
             case["bias_shape"] = [("B", "H", "Q", "K"), (1, 1, "Q", "K"), ("B", 1, 1, "K")][
                 int(rng.integers(0, 3))]
@@ -134,3 +135,66 @@ def test_random_case(case):
     fq, fk = d_rounding_floor(inp, to_np(o), lse_ref)
     for name, g, r, fl in zip(("dQ", "dK", "dV"), grads, ref, (fq, fk, None)):
         check_grad(to_np(g), r, f"{what} {name}", fl)
+
+
+# ------------------------------------------------------------ split-KV decode
+def _draw_decode(n=N_DECODE, seed=20261204):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 4, 8]))
+        nk = int(rng.integers(1, 3000))
+        B = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(0, nk + 1, size=B)]
+        cases.append(dict(id=c, B=B, Hq=hkv * g, Hkv=hkv, Nq=int(rng.integers(1, 5)), Nk=nk,
+                          d=int(rng.choice([64, 128])), lengths=lengths,
+                          causal=bool(rng.integers(0, 2)),
+                          window=int(rng.integers(1, 800)) if rng.random() < 0.3 else 0,
+                          splits=int(rng.integers(1, 40)) if rng.random() < 0.5 else None,
+                          noalloc=bool(rng.random() < 0.3), seed=2000 + c))
+    return cases
+
+
+DECODE_CASES = _draw_decode()
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"d{c['id']}" for c in DECODE_CASES])
+def test_random_decode(case):
+    """fa_decode (or fa_decode_noalloc) against attn_fwd on each sequence's
+    query rows and its first seqlens_k keys."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    what = (f"decode case {case['id']}: B={case['B']} Hq={case['Hq']} Hkv={case['Hkv']} "
+            f"Nq={case['Nq']} Nk={case['Nk']} d={case['d']} lengths={case['lengths']} "
+            f"causal={case['causal']} window={case['window']} splits={case['splits']} "
+            f"noalloc={case['noalloc']}")
+    say(f"[random] {what}")
+    inp = workloads.make_decode_inputs({k: case[k] for k in ("B", "Hq", "Hkv", "Nq", "Nk", "d",
+                                                            "lengths", "causal", "window",
+                                                            "seed")})
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    lens = torch.from_numpy(np.asarray(inp["seqlens_k"], np.int32)).cuda()
+    kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"], seqlens_k=lens)
+    if case["noalloc"]:
+        o = torch.empty_like(q)
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
+                          device="cuda")
+        fa.fa_decode_noalloc(q, k, v, out=o, lse=lse, num_splits=case["splits"] or 0, **kw)
+    else:
+        o, lse = fa.fa_decode(q, k, v, num_splits=case["splits"], **kw)
+    torch.cuda.synchronize()
+    o, lse = to_np(o), lse.cpu().numpy().astype(np.float64)
+    nq, hq, d = inp["q"].shape[1:]
+    for b in range(case["B"]):
+        L = int(inp["seqlens_k"][b])
+        if L == 0:
+            o_ref, l_ref = np.zeros((nq, hq, d)), np.full((hq, nq), -np.inf)
+        else:
+            o_ref, l_ref = oracle.attn_fwd(inp["q"][b:b + 1].astype(np.float64),
+                                           inp["k"][b:b + 1, :L].astype(np.float64),
+                                           inp["v"][b:b + 1, :L].astype(np.float64),
+                                           inp["scale"], inp["causal"], inp["window"])
+            o_ref, l_ref = o_ref[0], l_ref[0]
+        check_o(o[b], o_ref, f"{what} seq {b}")
+        check_lse(lse[b], l_ref, f"{what} seq {b}")
