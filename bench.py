@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--all] [--copy-calibration]
-    python bench.py --backward [--workload long_fwd_bwd] [--steps K] [--warmup W]
+    python bench.py --backward [--workload long_fwd_bwd] [--dtype bf16|f16] [--steps K]
+                    [--warmup W]
     python bench.py --decode [--steps K] [--warmup W]
 
 One step = one fa_fwd call over the whole workload: work partition, Q/K/V
@@ -220,7 +221,8 @@ def time_backward(inp, dev, steps, warmup):
     import exact_io_aware_28_amd as fa
     kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"],
               cu_seqlens=dev["cu"], max_seqlen=inp["Nq"] if dev["cu"] is not None else None)
-    fwd, bwd = fa.fa_fwd, fa.fa_bwd
+    fwd, bwd = {"bf16": (fa.fa_fwd, fa.fa_bwd), "f16": (fa.fa_fwd_f16, fa.fa_bwd_f16)}[
+        inp["dtype"]]
     if dev.get("bias") is not None:
         bias = dev["bias"]
         kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"])
@@ -232,7 +234,7 @@ def time_backward(inp, dev, steps, warmup):
         bwd = lambda q, k, v, o, do, lse, **a: fa.fa_bwd_dropout(q, k, v, o, do, lse, dp, ds,
                                                                  **a)
     o, lse = fwd(dev["q"], dev["k"], dev["v"], **kw)
-    do = torch.from_numpy(inp["do"]).to(torch.bfloat16).cuda()
+    do = torch.from_numpy(inp["do"]).to(dev["q"].dtype).cuda()
     dq, dk, dv = bwd(dev["q"], dev["k"], dev["v"], o, do, lse, **kw)
     ws = torch.empty(fa.fa_bwd_workspace_size(inp["B"] * inp["Nq"], inp["Hq"], inp["d"]),
                      dtype=torch.uint8, device="cuda")
@@ -361,6 +363,8 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time only the backward of --workload (default long_fwd_bwd)")
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default=None,
+                    help="with --backward: operand type (default: the workload's, bf16)")
     ap.add_argument("--decode", action="store_true",
                     help="time only the split-KV decode workload")
     a = ap.parse_args(argv)
@@ -390,13 +394,17 @@ def main(argv=None):
 
     if a.backward:
         name = a.workload if a.workload != "gqa_causal_prefill" else "long_fwd_bwd"
-        wi = workloads.make_inputs(name)
+        spec = dict(workloads.WORKLOADS[name])
+        if a.dtype:
+            spec["dtype"] = a.dtype
+        wi = workloads.make_inputs(spec)
         if not wi.get("bwd"):
             print(f"bench.py: workload {name} has no backward", file=sys.stderr)
             return 2
         bms = time_backward(wi, device_inputs(wi), a.steps, a.warmup)
         tf = 2.5 * attention_flops(wi) / (bms * 1e-3) / 1e12
-        print(json.dumps({"workload": name, "direction": "bwd", "steps": a.steps,
+        print(json.dumps({"workload": name, "direction": "bwd", "dtype": wi["dtype"],
+                          "steps": a.steps,
                           "warmup": a.warmup, "ms": round(bms, 4), "TFLOP/s": round(tf, 2),
                           "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
         return 0
@@ -473,6 +481,16 @@ def main(argv=None):
         print(json.dumps({"workload": a.workload, "direction": "fwd", "dtype": "f16",
                           "ms": round(wms, 4),
                           "TFLOP/s": round(attention_flops(wi) / (wms * 1e-3) / 1e12, 2)}),
+              flush=True)
+        del wd
+        torch.cuda.empty_cache()
+        # and the backward of the long workload with fp16 operands
+        wi = workloads.make_inputs(dict(workloads.WORKLOADS["long_fwd_bwd"], dtype="f16"))
+        wd = device_inputs(wi)
+        bms = time_backward(wi, wd, 5, 1)
+        print(json.dumps({"workload": "long_fwd_bwd", "direction": "bwd", "dtype": "f16",
+                          "ms": round(bms, 4),
+                          "TFLOP/s": round(2.5 * attention_flops(wi) / (bms * 1e-3) / 1e12, 2)}),
               flush=True)
         del wd
         torch.cuda.empty_cache()

@@ -90,6 +90,8 @@ def _load(path):
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                          i, i, i, i, i, i, f, i, i, vp, vp]
     L.fa_bwd.restype = i
+    L.fa_bwd_f16.argtypes = L.fa_bwd.argtypes
+    L.fa_bwd_f16.restype = i
     i64 = ctypes.c_int64
     L.fa_fwd_bias.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
                               vp, i64, i64, i64, vp]
@@ -315,16 +317,18 @@ def fa_fwd_dropout(q, k, v, dropout_p, seed, scale=None, causal=False, window=0,
 
 # ------------------------------------------------------------------ backward
 def _bwd_prepare(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, dq, dk, dv, workspace,
-                 stream, bias=None):
-    """Checks and outputs shared by the backward wrappers."""
+                 stream, bias=None, dtype=None):
+    """Checks and outputs shared by the backward wrappers (dtype: that of
+    q, k, v, o, dout and the gradients; bf16 unless given)."""
     import torch
-    B, hq, hkv, nq, nk, d = _geometry(q, k, v, cu_seqlens, max_seqlen, torch.bfloat16)
-    _tensor("o", o, torch.bfloat16, q.shape)
-    _tensor("dout", dout, torch.bfloat16, q.shape)
+    dt = torch.bfloat16 if dtype is None else dtype
+    B, hq, hkv, nq, nk, d = _geometry(q, k, v, cu_seqlens, max_seqlen, dt)
+    _tensor("o", o, dt, q.shape)
+    _tensor("dout", dout, dt, q.shape)
     _tensor("lse", lse, torch.float32, _lse_shape(q, B, hq, nq, cu_seqlens))
-    _optional("dq", dq, torch.bfloat16, q.shape)
-    _optional("dk", dk, torch.bfloat16, k.shape)
-    _optional("dv", dv, torch.bfloat16, v.shape)
+    _optional("dq", dq, dt, q.shape)
+    _optional("dk", dk, dt, k.shape)
+    _optional("dv", dv, dt, v.shape)
     ws_bytes = fa_bwd_workspace_size(B * nq, hq, d)
     _workspace(workspace, ws_bytes)
     bview = None if bias is None else _bias_view(bias, B, hq, nq, nk)
@@ -333,9 +337,9 @@ def _bwd_prepare(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, dq, dk, dv, work
                             ("dv", dv), ("workspace", workspace),
                             ("bias", None if bias is None else bias)])
     s = _launch_stream(stream)
-    dq = _alloc(dq, q.shape, torch.bfloat16, s, q.device)
-    dk = _alloc(dk, k.shape, torch.bfloat16, s, q.device)
-    dv = _alloc(dv, v.shape, torch.bfloat16, s, q.device)
+    dq = _alloc(dq, q.shape, dt, s, q.device)
+    dk = _alloc(dk, k.shape, dt, s, q.device)
+    dv = _alloc(dv, v.shape, dt, s, q.device)
     ws = _alloc(workspace, (max(ws_bytes, 1),), torch.uint8, s, q.device)
     return (B, hq, hkv, nq, nk, d), s, dq, dk, dv, ws, bview
 
@@ -358,6 +362,19 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
                                              dq, dk, dv, workspace, stream)
     args = [_ptr(x) for x in (q, k, v, o, dout, lse, dq, dk, dv, ws)] + [_nbytes(ws)]
     _bwd_call("fa_bwd", args, geo, scale, causal, window, [_ptr(cu_seqlens)], s)
+    return dq, dk, dv
+
+
+def fa_bwd_f16(q, k, v, o, dout, lse, scale=None, causal=False, window=0,
+               cu_seqlens=None, max_seqlen=None, dq=None, dk=None, dv=None,
+               workspace=None, stream=None):
+    """fp16 backward of fa_fwd_f16; returns (dq, dk, dv) in fp16."""
+    import torch
+    geo, s, dq, dk, dv, ws, _ = _bwd_prepare(q, k, v, o, dout, lse, cu_seqlens, max_seqlen,
+                                             dq, dk, dv, workspace, stream,
+                                             dtype=torch.float16)
+    args = [_ptr(x) for x in (q, k, v, o, dout, lse, dq, dk, dv, ws)] + [_nbytes(ws)]
+    _bwd_call("fa_bwd_f16", args, geo, scale, causal, window, [_ptr(cu_seqlens)], s)
     return dq, dk, dv
 
 

@@ -177,7 +177,7 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o,
                     int Nk, int d, float scale, int causal, int window,
                     const int32_t* cu_seqlens, const float* bias, int64_t sb, int64_t sh,
                     int64_t sq, int has_bias, void* stream, float dropout_p = 0.0f,
-                    uint64_t seed = 0) {
+                    uint64_t seed = 0, bool f16 = false) {
   const void* t[] = {q, k, v, o, dout, dq, dk, dv, workspace};
   const float* s[] = {lse};
   int st = check_common(t, 9, s, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, window,
@@ -225,7 +225,9 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o,
   p.window = window;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  return fa::launch_bwd_bf16(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const hipError_t e = f16 ? fa::launch_bwd_f16(p, (hipStream_t)stream)
+                           : fa::launch_bwd_bf16(p, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -234,6 +236,15 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int causal, int window, const int32_t* cu_seqlens, void* stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
                   Nq, Nk, d, scale, causal, window, cu_seqlens, nullptr, 0, 0, 0, 0, stream);
+}
+
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               float scale, int causal, int window, const int32_t* cu_seqlens, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                  Nq, Nk, d, scale, causal, window, cu_seqlens, nullptr, 0, 0, 0, 0, stream,
+                  0.0f, 0, true);
 }
 
 int fa_bwd_bias(const void* q, const void* k, const void* v, const void* o, const void* dout,

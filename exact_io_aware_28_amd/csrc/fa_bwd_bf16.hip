@@ -52,11 +52,20 @@ constexpr int kQBlock = 128;    // query rows per dQ work-group (4 waves x 32)
 constexpr int kKTile = 64;      // keys per staged tile in dQ
 constexpr int kReadsAhead = 4;  // LDS fragment reads issued ahead of the score MFMAs
 
+// Element e of eight 16-bit values held as raw bits (bf16, or fp16 with F16).
+template <bool F16>
+__device__ __forceinline__ float elem_f32(const bf16x8& v, int e) {
+  if constexpr (F16)
+    return (float)__builtin_bit_cast(f16x8, v)[e];
+  else
+    return (float)v[e];
+}
+
 // ------------------------------------------------------------ 1. D = dO . O
 // D/8 consecutive lanes share one (token, head) row: each reads 16 contiguous
 // bytes of O and of dO, so a wave instruction covers whole rows, and the
 // partial dot products are summed with lane shuffles inside the group.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams p) {
     const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>((const __bf16*)p.o + base));
     const bf16x8 g = as_bf16x8(*reinterpret_cast<const uint4*>((const __bf16*)p.dout + base));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)g[e], acc);
+    for (int e = 0; e < 8; ++e) acc = fmaf(elem_f32<F16>(a, e), elem_f32<F16>(g, e), acc);
   }
 #pragma unroll
   for (int m = kLanesPerRow / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -109,7 +118,7 @@ __device__ __forceinline__ uint32_t row_ror8(uint32_t x) {
 template <int D>
 constexpr int dkdv_waves_per_simd() { return D == 64 ? 2 : 1; }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP, bool F16>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(dkdv_waves_per_simd<D>())))
 void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
@@ -263,8 +272,8 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
         const uint32_t ro = qb * 32 * D * 2;
-        s = mfma32(as_bf16x8(lds_read_b128_at(tq, foff[st], ro)), kf[st], s);
-        dp = mfma32(as_bf16x8(lds_read_b128_at(tdo, foff[st], ro)), vf[st], dp);
+        s = mfma32_t<F16>(as_bf16x8(lds_read_b128_at(tq, foff[st], ro)), kf[st], s);
+        dp = mfma32_t<F16>(as_bf16x8(lds_read_b128_at(tdo, foff[st], ro)), vf[st], dp);
       }
 
       // Dropout keep bits of this lane's key for the block's 16 rows.  One
@@ -336,17 +345,17 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
         const int j = qc * 8;
-        const bf16x8 pb = pack_bf16x8(s[j], s[j + 1], s[j + 2], s[j + 3], s[j + 4],
+        const bf16x8 pb = pack8_t<F16>(s[j], s[j + 1], s[j + 2], s[j + 3], s[j + 4],
                                       s[j + 5], s[j + 6], s[j + 7]);
-        const bf16x8 dsb = pack_bf16x8(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
+        const bf16x8 dsb = pack8_t<F16>(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
                                        dp[j + 5], dp[j + 6], dp[j + 7]);
         const uint32_t ro = (qb * 32 + 16 * qc) * D * 2;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dva[db] = mfma32(cat(lds_read_tr_at(tdo, troff[0][db], ro),
+          dva[db] = mfma32_t<F16>(cat(lds_read_tr_at(tdo, troff[0][db], ro),
                                lds_read_tr_at(tdo, troff[1][db], ro)),
                            pb, dva[db]);
-          dka[db] = mfma32(cat(lds_read_tr_at(tq, troff[0][db], ro),
+          dka[db] = mfma32_t<F16>(cat(lds_read_tr_at(tq, troff[0][db], ro),
                                lds_read_tr_at(tq, troff[1][db], ro)),
                            dsb, dka[db]);
         }
@@ -387,15 +396,13 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        bf16x4 wk, wv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = (__bf16)(dka[db][4 * r + e] * p.scale);
-          wv[e] = (__bf16)(dva[db][4 * r + e]);
-        }
         const int col = db * 32 + r * 8 + hl * 4;
-        *reinterpret_cast<uint2*>(dkp + col) = __builtin_bit_cast(uint2, wk);
-        *reinterpret_cast<uint2*>(dvp + col) = __builtin_bit_cast(uint2, wv);
+        *reinterpret_cast<uint2*>(dkp + col) =
+            pack4_t<F16>(dka[db][4 * r] * p.scale, dka[db][4 * r + 1] * p.scale,
+                         dka[db][4 * r + 2] * p.scale, dka[db][4 * r + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dvp + col) =
+            pack4_t<F16>(dva[db][4 * r], dva[db][4 * r + 1], dva[db][4 * r + 2],
+                         dva[db][4 * r + 3]);
       }
   }
 }
@@ -412,7 +419,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
 // stay deterministic).
 constexpr int kDkdv8Threads = 512;
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP, bool F16>
 __global__ __launch_bounds__(kDkdv8Threads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
   constexpr int KS = D / 16, DB = D / 32;
@@ -556,9 +563,9 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
     for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
-      s = mfma32(as_bf16x8(lds_read_b128_at(tq, fq[st], 0)),
+      s = mfma32_t<F16>(as_bf16x8(lds_read_b128_at(tq, fq[st], 0)),
                  as_bf16x8(lds_read_b128_at(sk, fk[st], 0)), s);
-      dp = mfma32(as_bf16x8(lds_read_b128_at(tdo, fq[st], 0)),
+      dp = mfma32_t<F16>(as_bf16x8(lds_read_b128_at(tdo, fq[st], 0)),
                   as_bf16x8(lds_read_b128_at(sv, fk[st], 0)), dp);
     }
 
@@ -622,17 +629,17 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
       const int j = qc * 8;
-      const bf16x8 pb = pack_bf16x8(s[j], s[j + 1], s[j + 2], s[j + 3], s[j + 4],
+      const bf16x8 pb = pack8_t<F16>(s[j], s[j + 1], s[j + 2], s[j + 3], s[j + 4],
                                     s[j + 5], s[j + 6], s[j + 7]);
-      const bf16x8 dsb = pack_bf16x8(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
+      const bf16x8 dsb = pack8_t<F16>(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
                                      dp[j + 5], dp[j + 6], dp[j + 7]);
       const uint32_t ro = 16 * qc * D * 2;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32(cat(lds_read_tr_at(tdo, troff[0][db], ro),
+        dva[db] = mfma32_t<F16>(cat(lds_read_tr_at(tdo, troff[0][db], ro),
                              lds_read_tr_at(tdo, troff[1][db], ro)),
                          pb, dva[db]);
-        dka[db] = mfma32(cat(lds_read_tr_at(tq, troff[0][db], ro),
+        dka[db] = mfma32_t<F16>(cat(lds_read_tr_at(tq, troff[0][db], ro),
                              lds_read_tr_at(tq, troff[1][db], ro)),
                          dsb, dka[db]);
       }
@@ -697,10 +704,9 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const f32x4 o = xv[(db * 4 + r) * 64 + lane];
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(dva[db][4 * r + e] + o[e]);
-        *reinterpret_cast<uint2*>(dvp + db * 32 + r * 8 + hl * 4) = __builtin_bit_cast(uint2, w);
+        *reinterpret_cast<uint2*>(dvp + db * 32 + r * 8 + hl * 4) =
+            pack4_t<F16>(dva[db][4 * r] + o[0], dva[db][4 * r + 1] + o[1],
+                         dva[db][4 * r + 2] + o[2], dva[db][4 * r + 3] + o[3]);
       }
   } else {
     __bf16* dkp = (__bf16*)p.dk + off;
@@ -709,10 +715,10 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const f32x4 o = xk[(db * 4 + r) * 64 + lane];
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)((o[e] + dka[db][4 * r + e]) * p.scale);
-        *reinterpret_cast<uint2*>(dkp + db * 32 + r * 8 + hl * 4) = __builtin_bit_cast(uint2, w);
+        *reinterpret_cast<uint2*>(dkp + db * 32 + r * 8 + hl * 4) =
+            pack4_t<F16>((o[0] + dka[db][4 * r]) * p.scale, (o[1] + dka[db][4 * r + 1]) * p.scale,
+                         (o[2] + dka[db][4 * r + 2]) * p.scale,
+                         (o[3] + dka[db][4 * r + 3]) * p.scale);
       }
   }
 }
@@ -726,7 +732,7 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 template <int D, bool CAUSAL, bool WINDOW, bool BIAS>
 constexpr int dq_waves_per_simd() { return (D == 128 && !CAUSAL && !WINDOW) ? 1 : 2; }
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP, bool F16>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<D, CAUSAL, WINDOW, BIAS>())))
 void bwd_dq_kernel(BwdParams p, int num_qtiles) {
@@ -860,8 +866,8 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
         const uint32_t ro = kb * 32 * D * 2;
-        s = mfma32(as_bf16x8(lds_read_b128_at(kt, foff[st], ro)), qf[st], s);
-        dp = mfma32(as_bf16x8(lds_read_b128_at(vt, foff[st], ro)), dof[st], dp);
+        s = mfma32_t<F16>(as_bf16x8(lds_read_b128_at(kt, foff[st], ro)), qf[st], s);
+        dp = mfma32_t<F16>(as_bf16x8(lds_read_b128_at(vt, foff[st], ro)), dof[st], dp);
       }
       // a few fragment reads ahead of the MFMAs, then one read per MFMA
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsAhead, 0);
@@ -908,12 +914,12 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int kc = 2 * kb + h2, j = h2 * 8;
-        const bf16x8 dsb = pack_bf16x8(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
+        const bf16x8 dsb = pack8_t<F16>(dp[j], dp[j + 1], dp[j + 2], dp[j + 3], dp[j + 4],
                                        dp[j + 5], dp[j + 6], dp[j + 7]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const uint32_t ro = 16 * kc * D * 2;
-          acc[db] = mfma32(cat(lds_read_tr_at(kt, troff[0][db], ro),
+          acc[db] = mfma32_t<F16>(cat(lds_read_tr_at(kt, troff[0][db], ro),
                                lds_read_tr_at(kt, troff[1][db], ro)),
                            dsb, acc[db]);
         }
@@ -949,10 +955,9 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * r + e] * p.scale);
-        *reinterpret_cast<uint2*>(dqp + db * 32 + r * 8 + hl * 4) = __builtin_bit_cast(uint2, w);
+        *reinterpret_cast<uint2*>(dqp + db * 32 + r * 8 + hl * 4) =
+            pack4_t<F16>(acc[db][4 * r] * p.scale, acc[db][4 * r + 1] * p.scale,
+                         acc[db][4 * r + 2] * p.scale, acc[db][4 * r + 3] * p.scale);
       }
   }
 }
@@ -964,25 +969,29 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 template <int D, bool DROP>
 constexpr bool kUseDkdv8 = D == 128 && !DROP;
 
-template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false, bool DROP = false>
+template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false, bool DROP = false,
+          bool F16 = false>
 hipError_t launch4(const BwdParams& p, hipStream_t stream) {
   const int nkt = (p.Nk + kKeyBlock - 1) / kKeyBlock;
   const int nqt = (p.Nq + kQBlock - 1) / kQBlock;
   if constexpr (kUseDkdv8<D, DROP>)
-    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP, F16>),
                        dim3((unsigned)p.B * p.Hkv * nkt), dim3(kDkdv8Threads), 0, stream, p, nkt);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP, F16>),
                        dim3((unsigned)p.B * p.Hkv * nkt), dim3(kThreads), 0, stream, p, nkt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP>),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP, F16>),
                      dim3((unsigned)p.B * p.Hq * nqt), dim3(kThreads), 0, stream, p, nqt);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, bool CAUSAL, bool WINDOW, bool F16>
 hipError_t launch3(const BwdParams& p, hipStream_t stream) {
+  if constexpr (F16)  // fp16 operands: the plain backward only
+    return p.cu_seqlens ? launch4<D, CAUSAL, WINDOW, true, false, false, true>(p, stream)
+                        : launch4<D, CAUSAL, WINDOW, false, false, false, true>(p, stream);
   if (p.bias) return launch4<D, CAUSAL, WINDOW, false, true>(p, stream);  // dense only
   if (p.dropout)  // no bias
     return p.cu_seqlens ? launch4<D, CAUSAL, WINDOW, true, false, true>(p, stream)
@@ -991,25 +1000,29 @@ hipError_t launch3(const BwdParams& p, hipStream_t stream) {
                       : launch4<D, CAUSAL, WINDOW, false>(p, stream);
 }
 
-template <int D>
+template <int D, bool F16>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.Nq * p.Hq;  // >= tokens x heads, also when packed
   const int64_t rows_per_block = kThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>),
+  hipLaunchKernelGGL((bwd_pre_kernel<D, F16>),
                      dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                      dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool win = p.window > 0;
   if (p.causal)
-    return win ? launch3<D, true, true>(p, stream) : launch3<D, true, false>(p, stream);
-  return win ? launch3<D, false, true>(p, stream) : launch3<D, false, false>(p, stream);
+    return win ? launch3<D, true, true, F16>(p, stream) : launch3<D, true, false, F16>(p, stream);
+  return win ? launch3<D, false, true, F16>(p, stream) : launch3<D, false, false, F16>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
-  return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+  return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
+}
+
+hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t stream) {
+  return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
 }
 
 }  // namespace fa

@@ -120,6 +120,7 @@ hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_d128(const FwdParams& p, hipStream_t stream, bool f16);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t stream);  // plain only
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
 hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t stream);

@@ -155,6 +155,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const int32_t* cu_seqlens, void* stream);
 
 /*
+ * Backward of fa_fwd_f16: q, k, v, o, dout, dq, dk, dv are IEEE fp16, with
+ * the arguments, layouts, workspace and errors of fa_bwd (fa_fwd_f16 is the
+ * forward whose o and lse it takes).  The products run on fp16 matrix cores
+ * with fp32 accumulation; P and dS are rounded to fp16 (nearest even) as
+ * their operands, and D = rowsum(dO * O) is formed in fp32 from the fp16 O.
+ * Plain attention only (causal, window, GQA and packed batches as fa_bwd;
+ * no bias or dropout variant).
+ */
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               float scale, int causal, int window,
+               const int32_t* cu_seqlens, void* stream);
+
+/*
  * Forward and backward with an additive bias (a custom attention mask:
  * tokrepo.com "Flash Attention - Fast Memory-Efficient Exact Attention",
  * "Key Features"):  S = scale * Q K^T + bias, then the causal and window

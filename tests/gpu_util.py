@@ -45,13 +45,16 @@ def run_fwd(inp):
 
 
 def run_bwd(inp, dev):
+    """Call fa_bwd (fa_bwd_f16 for fp16 inputs) on the outputs of run_fwd."""
     import torch
     import exact_io_aware_28_amd as fa
-    do = to_dev(inp["do"])
+    dt = inp.get("dtype", "bf16")
+    do = to_dev(inp["do"], dt)
     cu = dev["cu"]
-    dq, dk, dv = fa.fa_bwd(dev["q"], dev["k"], dev["v"], dev["o"], do, dev["lse"],
-                           scale=inp["scale"], causal=inp["causal"], window=inp["window"],
-                           cu_seqlens=cu, max_seqlen=inp.get("Nq") if cu is not None else None)
+    fn = {"bf16": fa.fa_bwd, "f16": fa.fa_bwd_f16}[dt]
+    dq, dk, dv = fn(dev["q"], dev["k"], dev["v"], dev["o"], do, dev["lse"],
+                    scale=inp["scale"], causal=inp["causal"], window=inp["window"],
+                    cu_seqlens=cu, max_seqlen=inp.get("Nq") if cu is not None else None)
     torch.cuda.synchronize()
     return dq, dk, dv
 

@@ -11,6 +11,7 @@ hipError_t launch_fwd_f16(const FwdParams&, hipStream_t) { return hipErrorNotSup
 hipError_t launch_fwd_d128(const FwdParams&, hipStream_t, bool) { return hipErrorNotSupported; }
 hipError_t launch_fwd_f32(const FwdParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_bf16(const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_bwd_f16(const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_decode_bf16(const DecodeParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_fwd_fp8(const Fp8FwdParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quantize_fp8(const QuantParams&, hipStream_t) { return hipErrorNotSupported; }

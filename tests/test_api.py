@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_bias", "fa_bwd_dropout",
-                                    "fa_bwd_workspace_size",
+                                    "fa_bwd_f16", "fa_bwd_workspace_size",
                                     "fa_decode", "fa_decode_noalloc",
                                     "fa_decode_noalloc_max_splits", "fa_decode_num_splits",
                                     "fa_decode_workspace_size", "fa_fwd", "fa_fwd_bias",
@@ -105,17 +105,17 @@ def test_forward_rejects(entry, bad, code):
     assert _fwd(getattr(fa.lib(), entry), **bad) == code
 
 
-def _bwd(ws=P[9], ws_bytes=None, **kw):
+def _bwd(ws=P[9], ws_bytes=None, entry="fa_bwd", **kw):
     a = dict(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7],
              dv=P[8], B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125, causal=0,
              window=0, cu=None)
     a.update(kw)
     if ws_bytes is None:
         ws_bytes = fa.fa_bwd_workspace_size(a["B"] * a["Nq"], a["Hq"], a["d"])
-    return fa.lib().fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
-                           a["dk"], a["dv"], ws, ws_bytes, a["B"], a["Hq"], a["Hkv"],
-                           a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
-                           a["window"], a["cu"], None)
+    return getattr(fa.lib(), entry)(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                                    a["dq"], a["dk"], a["dv"], ws, ws_bytes, a["B"], a["Hq"],
+                                    a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                    a["causal"], a["window"], a["cu"], None)
 
 
 @pytest.mark.parametrize("bad,code", [
@@ -130,8 +130,9 @@ def _bwd(ws=P[9], ws_bytes=None, **kw):
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
     (dict(window=-3), fa.FA_ERR_INVALID_ARG),
 ])
-def test_backward_rejects(bad, code):
-    assert _bwd(**bad) == code
+@pytest.mark.parametrize("entry", ["fa_bwd", "fa_bwd_f16"])
+def test_backward_rejects(entry, bad, code):
+    assert _bwd(entry=entry, **bad) == code
 
 
 def test_workspace_is_linear_in_rows():
@@ -329,8 +330,8 @@ def test_valid_calls_reach_the_launcher():
     parameter block and returns the launcher's failure as FA_ERR_HIP: the
     whole host path of each entry point runs under the sanitizer."""
     L = fa.lib()
-    for call in (lambda: _fwd(), lambda: _bwd(), lambda: _dec(), lambda: _fwd_bias(),
-                 lambda: _bwd_bias()):
+    for call in (lambda: _fwd(), lambda: _bwd(), lambda: _bwd(entry="fa_bwd_f16"),
+                 lambda: _dec(), lambda: _fwd_bias(), lambda: _bwd_bias()):
         assert call() == fa.FA_ERR_HIP
     assert L.fa_quantize_fp8(P[0], P[1], P[2], 2, 100, 3, 128, 1, P[3], None) == fa.FA_ERR_HIP
     assert L.fa_fwd_fp8(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 1, 4, 2, 100, 100, 128,

@@ -100,9 +100,11 @@ def bwd_args():
     return q, k, v, o, do, lse
 
 
-@pytest.mark.parametrize("fn", ["fa_bwd", "fa_bwd_dropout"])
+@pytest.mark.parametrize("fn", ["fa_bwd", "fa_bwd_dropout", "fa_bwd_f16"])
 def test_backward_checks(fn):
     q, k, v, o, do, lse = bwd_args()
+    if fn == "fa_bwd_f16":
+        q, k, v, o, do = (t.half() for t in (q, k, v, o, do))
     extra = (0.1, 5) if fn == "fa_bwd_dropout" else ()
     f = getattr(fa, fn)
     raises(ValueError, "o must have shape", f, q, k, v, o[:, :32].contiguous(), do, lse, *extra)
@@ -117,6 +119,15 @@ def test_backward_checks(fn):
            workspace=torch.empty(8, dtype=torch.uint8))
     raises(ValueError, "same shape", f, q, k, v[:, :, :1].contiguous(), o, do, lse, *extra)
     raises(ValueError, "device tensor", f, q, k, v, o, do, lse, *extra)
+
+
+def test_f16_backward_wants_half_everywhere():
+    q, k, v, o, do, lse = bwd_args()
+    raises(TypeError, "must be torch.float16", fa.fa_bwd_f16, q, k, v, o, do, lse)
+    h = [t.half() for t in (q, k, v, o, do)]
+    raises(TypeError, "dout must be torch.float16", fa.fa_bwd_f16, *h[:4], do, lse)
+    raises(TypeError, "dq must be torch.float16", fa.fa_bwd_f16, *h, lse,
+           dq=torch.empty_like(q))
 
 
 def test_backward_packed_checks_cu_seqlens():
