@@ -95,6 +95,20 @@ __device__ __forceinline__ float fast_exp2(float x) {
 // Value of lane (l ^ 32): the other half of the wave.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max(x, x of lane l ^ 32) and x + (x of lane l ^ 32) in every lane, with one
+// v_permlane32_swap (a vector ALU exchange of the two half-waves) instead of
+// the LDS crossbar that a general shuffle uses.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // A K or V tile of R rows x D bf16 columns is stored row-major with its
 // 16-byte chunks permuted inside each row: chunk c of row r lives at chunk

@@ -161,7 +161,21 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m_run = -kInf;  // reference maximum, scaled (log2) units
   float l_run = 0.f;    // this half-wave's share of the normaliser
-  const float c = p.scale_log2;
+  // The tile loop always takes the row maximum with a positive multiplier,
+  // so it has no branch between the score products and the softmax: a
+  // negative scale is applied as |scale| to -Q (flipping the sign bits is
+  // exact), and a zero scale becomes a tiny positive one, with which every
+  // exp2(s c - m) still rounds to exactly 1 and a masked score (the -inf
+  // sentinel) exponentiates to exactly 0 rather than to NaN.
+  float c = p.scale_log2;
+  if (c < 0.f) {
+    c = -c;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = as_bf16x8(__builtin_bit_cast(uint4, qf[s]) ^
+                        make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u));
+  }
+  if (c == 0.f) c = 1e-30f;
   // with a bias the scores are turned into log2 units right after the
   // product, and the softmax update below multiplies by 1
   const float cs = BIAS ? 1.0f : c;
@@ -255,11 +269,10 @@ void fwd_bf16_kernel(FwdParams p) {
     }
 
     // Online-softmax update and P V product.  MASKED tiles straddle a mask
-    // boundary: an invisible score is replaced by a sentinel that never wins
-    // the row extreme, and its probability is forced to zero.
+    // boundary: an invisible score is replaced by -inf, which never wins the
+    // row maximum and whose probability exp2(-inf) is exactly zero.
     auto softmax_tile = [&](auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      const float sentinel = (cs >= 0.f) ? -kInf : kInf;
       auto key_of = [&](int kb, int i) { return j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3); };
       if (MASKED) {
 #pragma unroll
@@ -267,23 +280,15 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (!visible<CAUSAL, WINDOW>(qi, key_of(kb, i), delta, sp.lk, p.window))
-              s[kb][i] = sentinel;
+              s[kb][i] = -kInf;
       }
-      // row extreme of the raw scores (max for c >= 0, min for c < 0)
+      // row maximum of the raw scores (the multiplier cs is positive)
       float rm = s[0][0];
-      if (cs >= 0.f) {
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) rm = fmaxf(rm, s[kb][i]);
-        rm = fmaxf(rm, xor32(rm));
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) rm = fminf(rm, s[kb][i]);
-        rm = fminf(rm, xor32(rm));
-      }
+        for (int i = 0; i < 16; ++i) rm = fmaxf(rm, s[kb][i]);
+      rm = max_halves(rm);
       const float tmax = __builtin_isinf(rm) ? -kInf : rm * cs;
 
       float m_use = m_run;
@@ -315,10 +320,7 @@ void fwd_bf16_kernel(FwdParams p) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(s[kb][i0 + e], cs, neg));
-          if (MASKED)
-            pv[e] = visible<CAUSAL, WINDOW>(qi, key_of(kb, i0 + e), delta, sp.lk, p.window)
-                        ? pv[e] : 0.f;
+          pv[e] = fast_exp2(fmaf(s[kb][i0 + e], cs, neg));  // 0 for a masked score
           if (e & 1)
             lsum1 += pv[e];
           else
@@ -359,7 +361,7 @@ void fwd_bf16_kernel(FwdParams p) {
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   if (qi < sp.lq) {
     // dropout scales the kept probabilities by 1 / (1 - p)
     const float inv = (l_tot == 0.f) ? 0.f : (DROP ? p.drop_scale : 1.0f) / l_tot;
