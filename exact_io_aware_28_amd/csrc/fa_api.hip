@@ -70,6 +70,7 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.num_qtiles = 0;  // set by the launcher from its tile height
+  p.xcd_groups = 0;
   p.bias = nullptr;
   p.bias_sb = p.bias_sh = p.bias_sq = 0;
   p.dropout = 0;

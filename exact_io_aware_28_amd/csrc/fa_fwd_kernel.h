@@ -92,6 +92,14 @@ void fwd_bf16_kernel(FwdParams p) {
   // ---- which (sequence, head, query block) this work-group computes
   uint32_t id = xcd_logical_id(blockIdx.x, gridDim.x);
   const int G = p.group;
+  if (CAUSAL && p.xcd_groups > 1) {
+    // Each XCD's contiguous range holds whole KV-head groups; run their
+    // longest query tiles first across all of them instead of group by group,
+    // so that no long tile starts near the end of a short grid.
+    const uint32_t per = gridDim.x / kNumXcd, x = id / per, u = id % per;
+    const uint32_t g = (uint32_t)G, K = (uint32_t)p.xcd_groups, rest = u / g;
+    id = x * per + u % g + g * (rest / K + (uint32_t)p.num_qtiles * (rest % K));
+  }
   const int gi = id % G;
   id /= G;
   int t_ord, b, hkv;
@@ -405,6 +413,17 @@ template <int D, int W, bool CAUSAL, bool WINDOW, bool VARLEN, bool F16, bool BI
           bool DROP = false>
 hipError_t launch_w(FwdParams p, hipStream_t stream) {
   p.num_qtiles = (p.Nq + 32 * W - 1) / (32 * W);
+  // Causal dense grids of at most about two rounds of work-groups per XCD
+  // finish sooner with each XCD's longest query tiles dispatched first (a
+  // bigger grid balances by itself and keeps its head-major order).
+  p.xcd_groups = 0;
+  if (CAUSAL && !VARLEN && !(BIAS && p.bias_sh == 0)) {
+    const long n = (long)p.B * p.Hq * p.num_qtiles, per = n / kNumXcd;
+    const long unit = (long)p.group * p.num_qtiles;     // work-groups of one KV head
+    const long slots = 32L * (D == 64 ? 3 : 1);          // resident per XCD: 32 CUs
+    if (n % kNumXcd == 0 && per % unit == 0 && per / unit > 1 && per <= 2 * slots)
+      p.xcd_groups = (int)(per / unit);
+  }
   dim3 grid((unsigned)p.B * p.Hq * p.num_qtiles), block(64 * W);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, W, CAUSAL, WINDOW, VARLEN, F16, BIAS, DROP>), grid,
                      block, 0, stream, p);

@@ -23,6 +23,8 @@ struct FwdParams {
   float scale;                // multiplier of Q K^T
   float scale_log2;           // scale * log2(e): exp(x*scale) = exp2(x*scale_log2)
   int num_qtiles;             // ceil(Nq / query-tile rows) of the kernel
+  int xcd_groups;             // > 1: each XCD runs the longest query tiles of its
+                              // xcd_groups KV-head groups first (set by the launcher)
   // additive bias of dense batches, nullptr when there is none: element
   // (b, h, i, j) at bias[b*bias_sb + h*bias_sh + i*bias_sq + j]
   const float* bias;
