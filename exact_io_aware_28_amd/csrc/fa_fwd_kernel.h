@@ -227,9 +227,7 @@ void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  auto compute = [&](int j0, const __bf16* kt, const __bf16* vt, auto may_mask_tag)
-                     __attribute__((always_inline)) {
-    constexpr bool MAY_MASK = decltype(may_mask_tag)::value;
+  auto compute = [&](int j0, const __bf16* kt, const __bf16* vt) __attribute__((always_inline)) {
     bool active = qlo_w <= qhi_w;
     if (CAUSAL) active = active && (j0 <= qhi_w + delta);
     if (WINDOW) active = active && (j0 + kBN - 1 > qlo_w + delta - p.window);
@@ -278,20 +276,24 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(bt[kb * 16 + i], kLog2e, s[kb][i] * c);
     }
 
-    // Online-softmax update and P V product.  MASKED tiles straddle a mask
-    // boundary: an invisible score is replaced by -inf, which never wins the
-    // row maximum and whose probability exp2(-inf) is exactly zero.
-    auto softmax_tile = [&](auto masked_tag) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      auto key_of = [&](int kb, int i) { return j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3); };
-      if (MASKED) {
+    // A tile that straddles a mask boundary first replaces each invisible
+    // score by -inf, which never wins the row maximum and whose probability
+    // exp2(-inf) is exactly zero; then every tile takes the same update.  The
+    // masking stays a separate, rarely taken block: with a second full copy
+    // of the update for masked tiles the compiler moved the accumulators
+    // between register sets or spilled, and if-converted it would run the
+    // selects on every tile.
+    auto key_of = [&](int kb, int i) { return j0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3); };
+    if (__builtin_expect(need_mask, 0)) {
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (!visible<CAUSAL, WINDOW>(qi, key_of(kb, i), delta, sp.lk, p.window))
-              s[kb][i] = -kInf;
-      }
+        for (int i = 0; i < 16; ++i)
+          if (!visible<CAUSAL, WINDOW>(qi, key_of(kb, i), delta, sp.lk, p.window))
+            s[kb][i] = -kInf;
+    }
+    // Online-softmax update and P V product.
+    {
       // row maximum of the raw scores (the multiplier cs is positive)
       float rm = s[0][0];
 #pragma unroll
@@ -348,41 +350,22 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int db = 0; db < DB; ++db) acc[db] = mfma32_t<F16>(va[db], pb, acc[db]);
       }
       l_run += lsum0 + lsum1;
-    };
-    if (MAY_MASK && need_mask)
-      softmax_tile(std::true_type{});
-    else
-      softmax_tile(std::false_type{});
+    }
   };
 
   // ---- main loop over K/V tiles, two buffers (unrolled by two)
-  auto main_loop = [&](auto may_mask_tag) __attribute__((always_inline)) {
-    for (int j0 = kv_lo; j0 < kv_hi; j0 += 2 * kBN) {
-      dma_barrier();  // tile j0 is in buffer 0; buffer 1 is free
-      if (j0 + kBN < kv_hi) issue(j0 + kBN, k1, v1);
-      FA_STAGE_SYNC();
-      compute(j0, k0, v0, may_mask_tag);
-      FA_STAGE_SYNC();
-      if (j0 + kBN >= kv_hi) break;
-      dma_barrier();  // tile j0 + kBN is in buffer 1; buffer 0 is free
-      if (j0 + 2 * kBN < kv_hi) issue(j0 + 2 * kBN, k0, v0);
-      FA_STAGE_SYNC();
-      compute(j0 + kBN, k1, v1, may_mask_tag);
-      FA_STAGE_SYNC();
-    }
-  };
-  // Without a causal or window mask only a ragged last tile needs the masked
-  // body.  At d = 64 a sequence whose key count is a multiple of the tile
-  // runs a second copy of the loop without it: with both bodies in one loop
-  // the compiler copies the accumulators between register sets on every
-  // tile.  (At d = 128 the second copy costs spills instead.)
-  if constexpr (D == 64 && !CAUSAL && !WINDOW) {
-    if (sp.lk % kBN == 0)
-      main_loop(std::false_type{});
-    else
-      main_loop(std::true_type{});
-  } else {
-    main_loop(std::true_type{});
+  for (int j0 = kv_lo; j0 < kv_hi; j0 += 2 * kBN) {
+    dma_barrier();  // tile j0 is in buffer 0; buffer 1 is free
+    if (j0 + kBN < kv_hi) issue(j0 + kBN, k1, v1);
+    FA_STAGE_SYNC();
+    compute(j0, k0, v0);
+    FA_STAGE_SYNC();
+    if (j0 + kBN >= kv_hi) break;
+    dma_barrier();  // tile j0 + kBN is in buffer 1; buffer 0 is free
+    if (j0 + 2 * kBN < kv_hi) issue(j0 + 2 * kBN, k0, v0);
+    FA_STAGE_SYNC();
+    compute(j0 + kBN, k1, v1);
+    FA_STAGE_SYNC();
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l)
