@@ -304,23 +304,39 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
           kw[v] = (((v >> 2) == a) ? own_w[v & 3] : oth_w[v & 3]) >> u;
       }
 
-      auto grads = [&](auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
+      // P for every element; a block that straddles a mask boundary then
+      // zeroes its invisible entries in a separate, rarely taken step, and one
+      // update forms dS for every block (with a second full copy of the update
+      // for masked blocks the dropout backward ran 3 % slower)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 L = *reinterpret_cast<const float4*>(&tl[qb * 32 + 8 * r + 4 * hl]);
+        const float Lv[4] = {L.x, L.y, L.z, L.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r + e;
+          float pv = fmaf(s[i], c, -Lv[e]);
+          if constexpr (BIAS) pv = fmaf(bv[i], kLog2e, pv);
+          s[i] = fast_exp2(pv);
+        }
+      }
+      if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qr = qb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (!visible<CAUSAL, WINDOW>(i0 + qr, kj, delta, sp.lk, p.window)) s[i] = 0.f;
+        }
+      }
+      {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qrow = qb * 32 + 8 * r + 4 * hl;
-          const float4 L = *reinterpret_cast<const float4*>(&tl[qrow]);
           const float4 Dl = *reinterpret_cast<const float4*>(&td[qrow]);
-          const float Lv[4] = {L.x, L.y, L.z, L.w};
           const float Dv[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * r + e;
-            float pv = fmaf(s[i], c, -Lv[e]);
-            if constexpr (BIAS) pv = fmaf(bv[i], kLog2e, pv);
-            pv = fast_exp2(pv);
-            if (MASKED)
-              pv = visible<CAUSAL, WINDOW>(i0 + qrow + e, kj, delta, sp.lk, p.window) ? pv : 0.f;
+            const float pv = s[i];
             if constexpr (DROP) {
               // O = (P Z / (1 - p)) V: dV takes the dropped, rescaled P and
               // the gradient reaching P is dP Z / (1 - p)
@@ -334,11 +350,7 @@ void bwd_dkdv_kernel(BwdParams p, int num_ktiles) {
             }
           }
         }
-      };
-      if (need_mask)
-        grads(std::true_type{});
-      else
-        grads(std::false_type{});
+      }
 
       // dV^T += dO^T P and dK^T += Q^T dS over 16-query chunks; chunk qc
       // holds queries 16qc + 4hl + {0..3} and 16qc + 8 + 4hl + {0..3}
