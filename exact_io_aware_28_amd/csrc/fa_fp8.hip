@@ -177,7 +177,16 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
       for (int e = 0; e < 8; ++e) qf[st][e] = 0;
   }
   const int qblk = min((q_start + wave * 32) / kBN8, p.nbq - 1);
-  const float c_q = p.scale_log2 * p.sq[((int64_t)b * p.Hq + h) * p.nbq + qblk];
+  // The tile loop always takes the row maximum with a positive multiplier:
+  // a negative scale is applied as |scale| to -Q (the E4M3 sign bits
+  // flipped, exact), so no runtime branch separates the score products from
+  // the softmax.
+  float c_q = p.scale_log2 * p.sq[((int64_t)b * p.Hq + h) * p.nbq + qblk];
+  if (c_q < 0.f) {
+    c_q = -c_q;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qf[st] = qf[st] ^ (int)0x80808080u;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -208,7 +217,10 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
     if (CAUSAL) need_mask = need_mask || (j0 + kBN8 - 1 > qlo_w + delta);
     if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
     const int tile = j0 / kBN8;
-    const float cs = c_q * skp[tile];                 // score -> log2 units
+    // score -> log2 units; kept >= 1e-30 so that a masked score (-inf)
+    // exponentiates to exactly 0 even if the product underflows (with it
+    // every exp2(s cs - m) of such a tile still rounds as with cs = 0)
+    const float cs = fmaxf(c_q * skp[tile], 1e-30f);
     const float lr = __log2f(svp[tile]) - lsref;      // <= 0: this tile's V scale
     const float lsc = fast_exp2(-lr);                 // sV_ref / sV(tile)
 
@@ -228,32 +240,25 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
         s[kb] = mfma_fp8(a, qf[st], s[kb]);
       }
 
-    auto softmax_tile = [&](auto masked_tag) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      const float sentinel = (cs >= 0.f) ? -kInf : kInf;
-      auto key_of = [&](int kb, int i) { return j0 + 32 * hl + 16 * kb + i; };
-      if (MASKED) {
+    // A tile that straddles a mask boundary first sets each invisible score
+    // to -inf (never the row maximum; exp2 of it is exactly 0), in a
+    // separate, rarely taken block; then every tile takes the same update.
+    auto key_of = [&](int kb, int i) { return j0 + 32 * hl + 16 * kb + i; };
+    if (__builtin_expect(need_mask, 0)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (!visible<CAUSAL, WINDOW>(qi, key_of(kb, i), delta, p.Nk, p.window))
-              s[kb][i] = sentinel;
-      }
+        for (int i = 0; i < 16; ++i)
+          if (!visible<CAUSAL, WINDOW>(qi, key_of(kb, i), delta, p.Nk, p.window))
+            s[kb][i] = -kInf;
+    }
+    {
       float rm = s[0][0];
-      if (cs >= 0.f) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) rm = fmaxf(rm, s[kb][i]);
-        rm = fmaxf(rm, xor32(rm));
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) rm = fminf(rm, s[kb][i]);
-        rm = fminf(rm, xor32(rm));
-      }
+        for (int i = 0; i < 16; ++i) rm = fmaxf(rm, s[kb][i]);
+      rm = max_halves(rm);
       const float tmax = __builtin_isinf(rm) ? -kInf : rm * cs;
       float m_use = m_run;
       if (tmax > m_run + kSlack8) m_use = tmax;  // also when m_run = -inf
@@ -278,12 +283,7 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
         for (int i = 0; i < 16; i += 4) {
           float e[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            e[u] = fast_exp2(fmaf(s[kb][i + u], cs, neg));
-            if (MASKED)
-              e[u] = visible<CAUSAL, WINDOW>(qi, key_of(kb, i + u), delta, p.Nk, p.window)
-                         ? e[u] : 0.f;
-          }
+          for (int u = 0; u < 4; ++u) e[u] = fast_exp2(fmaf(s[kb][i + u], cs, neg));
           lsum0 += e[0] + e[2];
           lsum1 += e[1] + e[3];
           pk[kb * 4 + i / 4] = pack_fp8x4(e[0], e[1], e[2], e[3]);
@@ -296,11 +296,7 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
                              lds_read_b128_at((const __bf16*)vt, voff[1], rows));
         acc[db] = mfma_fp8(a, pk, acc[db]);
       }
-    };
-    if (need_mask)
-      softmax_tile(std::true_type{});
-    else
-      softmax_tile(std::false_type{});
+    }
   };
 
   // ---- main loop over K/V tiles, two buffers
@@ -319,7 +315,7 @@ void fwd_fp8_kernel(Fp8FwdParams p) {
   }
 
   // ---- epilogue: O = acc * sV_ref / l', LSE = ln 2 * (m + log2 l' - 7)
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   if (qi < p.Nq) {
     const float inv = (l_tot == 0.f) ? 0.f : sref / l_tot;
     __bf16* op = (__bf16*)p.o + (((int64_t)b * p.Nq + qi) * p.Hq + h) * D;

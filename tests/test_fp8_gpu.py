@@ -155,12 +155,27 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
 def test_fwd_fp8_parity(case):
+    _fp8_parity(case)
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_fwd_fp8_scale_sign(scale):
+    """A negative scale (the kernel applies |scale| to -Q) and a zero scale
+    (uniform weights over the visible keys)."""
+    _fp8_parity((1, 300, 300, 4, 2, 128, True, 40), scale)
+
+
+def _fp8_parity(case, scale=None):
     import torch
     import exact_io_aware_28_amd as fa
     B, Nq, Nk, Hq, Hkv, d, causal, window = case
-    inp = workloads.make_fp8_inputs(dict(B=B, Nq=Nq, Nk=Nk, Hq=Hq, Hkv=Hkv, d=d, causal=causal,
-                                         window=window, seed=600 + Nq + Nk))
-    what = f"B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} window={window}"
+    spec = dict(B=B, Nq=Nq, Nk=Nk, Hq=Hq, Hkv=Hkv, d=d, causal=causal, window=window,
+                seed=600 + Nq + Nk)
+    inp = workloads.make_fp8_inputs(spec)
+    if scale is not None:
+        inp["scale"] = scale
+    what = (f"B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} causal={causal} window={window} "
+            f"scale={inp['scale']:.4g}")
     say(f"[fp8 fwd] {what}")
     q8, k8, vt8, sq, sk, sv = _fp8_dev(inp)
     o, lse = fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, scale=inp["scale"], causal=causal,
