@@ -110,11 +110,12 @@ def check_grad(g, ref, what="", floor=None):
     return mx / max(scale, 1e-30)
 
 
-def d_rounding_floor(inp, o, lse_ref):
+def d_rounding_floor(inp, o, lse_ref, unit=2.0 ** -9):
     """Elementwise first-order bound of the dQ and dK error that comes from
     forming D_i = sum_c dO_ic O_ic from the bf16 O the backward receives (the
     exact gradients use the exact O).  Rounding O to bf16 (to nearest) moves
-    D_i by at most e_i = 2^-9 sum_c |dO_ic O_ic|; through
+    D_i by at most e_i = unit sum_c |dO_ic O_ic| (unit = 2^-9, half a bf16
+    step; 2^-12 for an fp16 O); through
     dS_ij = P_ij (dP_ij - D_i) that moves dQ_ic by at most
     scale e_i sum_j P_ij |K_jc|, and dK_jc by at most
     scale sum_i P_ij e_i |Q_ic| (summed over the query heads of the KV head).
@@ -156,7 +157,7 @@ def d_rounding_floor(inp, o, lse_ref):
             fin = np.isfinite(l)[:, None] & ok
             with np.errstate(invalid="ignore", over="ignore"):  # rows that see no key
                 p = np.where(fin, np.exp(np.where(fin, s - l[:, None], -np.inf)), 0.0)
-            e_i = 2.0 ** -9 * np.abs(dos[:, h] * os_[:, h]).sum(axis=1)
+            e_i = unit * np.abs(dos[:, h] * os_[:, h]).sum(axis=1)
             fq_h = scale * e_i[:, None] * (p @ np.abs(ks[:, kv]))
             fk_h = scale * (p * e_i[:, None]).T @ np.abs(qs[:, h])
             if span is None:

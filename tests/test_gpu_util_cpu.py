@@ -1,6 +1,7 @@
 """CPU checks of the derived gradient floor the GPU tests use
 (tests/gpu_util.d_rounding_floor): the first-order bound of the dQ/dK error
-that forming D = rowsum(dO * O) from the bf16-rounded O causes.
+that forming D = rowsum(dO * O) from the rounded O (bf16, or fp16 for the
+fp16 path) causes.
 
 The backward is emulated in fp64 from its definition with exactly that one
 change (D from round_bf16(O)); its difference from the exact gradients must
@@ -42,20 +43,28 @@ def _emulated_grads(inp, o_rounded):
     return dq, dk
 
 
+ROUNDINGS = {  # dtype: (rounding of O to nearest, unit of d_rounding_floor)
+    "bf16": (lambda x: workloads.round_bf16(x.astype(np.float32)), 2.0 ** -9),
+    "f16": (lambda x: x.astype(np.float16), 2.0 ** -12),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("spec", [
     dict(B=1, Nq=70, Nk=70, Hq=2, Hkv=1, d=64, causal=True, window=0, seed=41),
     dict(B=2, Nq=33, Nk=90, Hq=4, Hkv=2, d=32, causal=True, window=20, seed=42),
     dict(B=1, Nq=50, Nk=50, Hq=2, Hkv=2, d=16, causal=False, window=0, seed=43),
 ])
-def test_floor_bounds_the_rounded_o_effect(spec):
-    inp = workloads.make_inputs(dict(spec, bwd=True))
+def test_floor_bounds_the_rounded_o_effect(spec, dtype):
+    round_o, unit = ROUNDINGS[dtype]
+    inp = workloads.make_inputs(dict(spec, bwd=True, dtype=dtype))
     f = lambda n: inp[n].astype(np.float64)
     o, lse = oracle.attn_fwd(f("q"), f("k"), f("v"), inp["scale"], inp["causal"], inp["window"])
-    o_r = workloads.round_bf16(o.astype(np.float32)).astype(np.float64)
+    o_r = round_o(o).astype(np.float64)
     dq, dk, _ = oracle.attn_bwd(f("q"), f("k"), f("v"), f("do"), inp["scale"], inp["causal"],
                                 inp["window"])
     edq, edk = _emulated_grads(inp, o_r)
-    fq, fk = d_rounding_floor(inp, o_r, lse)
+    fq, fk = d_rounding_floor(inp, o_r, lse, unit)
     for name, err, fl in (("dQ", np.abs(edq - dq), fq), ("dK", np.abs(edk - dk), fk)):
         # inside the bound (first order: allow 1 % for the second-order terms)
         assert np.all(err <= 1.01 * fl + 1e-12), (name, float((err - fl).max()))

@@ -10,7 +10,8 @@ compared at the bars of tests/gpu_util.py (the derived dropout bar for O,
 and for dQ and dK the bound of the error that forming D from the bf16 O
 carries, which decides only where the exact gradient vanishes).
 The configurations come from one fixed generator seed, so a failure names a
-case that reproduces.
+case that reproduces.  A second draw runs plain attention in fp16 through
+fa_fwd_f16 and fa_bwd_f16, and a third the split-KV decode.
 """
 
 import numpy as np
@@ -25,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 40
 N_DECODE = 16
+N_F16 = 12
 
 
 def _draw_cases(n=N_CASES, seed=20261203):
@@ -133,6 +135,70 @@ def test_random_case(case):
     # dQ and dK may also differ by the error of forming D from the bf16 O
     # (d_rounding_floor); it decides only where the exact gradient vanishes
     fq, fk = d_rounding_floor(inp, to_np(o), lse_ref)
+    for name, g, r, fl in zip(("dQ", "dK", "dV"), grads, ref, (fq, fk, None)):
+        check_grad(to_np(g), r, f"{what} {name}", fl)
+
+
+# ------------------------------------------------------------ fp16 operands
+def _draw_f16(n=N_F16, seed=20261205):
+    """Plain attention in IEEE half (fa_fwd_f16 / fa_bwd_f16): the same
+    mix of shapes, masks, GQA groups and packing as the bf16 draw."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        hkv = int(rng.choice([1, 2]))
+        case = dict(id=c, d=int(rng.choice([64, 128])), Hkv=hkv,
+                    Hq=hkv * int(rng.choice([1, 2, 4, 8])), causal=bool(rng.integers(0, 2)),
+                    window=int(rng.integers(1, 200)) if rng.random() < 0.3 else 0,
+                    seed=3000 + c)
+        if rng.random() < 0.3:
+            case["lengths"] = [int(x) for x in rng.integers(0, 260, size=int(rng.integers(1, 5)))]
+        else:
+            case["B"] = int(rng.integers(1, 4))
+            case["Nq"] = int(rng.integers(1, 520))
+            case["Nk"] = case["Nq"] if rng.random() < 0.6 else int(rng.integers(1, 520))
+        cases.append(case)
+    return cases
+
+
+F16_CASES = _draw_f16()
+
+
+@pytest.mark.parametrize("case", F16_CASES, ids=[f"h{c['id']}" for c in F16_CASES])
+def test_random_f16(case):
+    """O, LSE, dQ, dK, dV in fp16 against the oracle on the fp16-rounded
+    inputs, at the bars of the bf16 sweep (the D floor with fp16's unit)."""
+    import torch
+    import exact_io_aware_28_amd as fa
+    shape = (f"lengths={case['lengths']}" if "lengths" in case
+             else f"B={case['B']} Nq={case['Nq']} Nk={case['Nk']}")
+    what = (f"f16 case {case['id']}: {shape} Hq={case['Hq']} Hkv={case['Hkv']} d={case['d']} "
+            f"causal={case['causal']} window={case['window']}")
+    say(f"[random] {what}")
+    spec = {k: case[k] for k in ("Hq", "Hkv", "d", "causal", "window", "seed")}
+    spec.update(bwd=True, dtype="f16")
+    if "lengths" in case:
+        spec["lengths"] = case["lengths"]
+    else:
+        spec.update(B=case["B"], Nq=case["Nq"], Nk=case["Nk"])
+    inp = workloads.make_inputs(spec)
+    q, k, v, do = (to_dev(inp[n], "f16") for n in ("q", "k", "v", "do"))
+    cu = inp.get("cu_seqlens")
+    cu_t = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    kw = dict(scale=inp["scale"], causal=inp["causal"], window=inp["window"], cu_seqlens=cu_t,
+              max_seqlen=inp["Nq"] if cu is not None else None)
+    o, lse = fa.fa_fwd_f16(q, k, v, **kw)
+    grads = fa.fa_bwd_f16(q, k, v, o, do, lse, **kw)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16 and all(g.dtype == torch.float16 for g in grads)
+    f = lambda n: inp[n].astype(np.float64)
+    o_ref, lse_ref = oracle.attn_fwd(f("q"), f("k"), f("v"), inp["scale"], inp["causal"],
+                                     inp["window"], cu)
+    check_o(to_np(o), o_ref, what)
+    check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, what)
+    ref = oracle.attn_bwd(f("q"), f("k"), f("v"), f("do"), inp["scale"], inp["causal"],
+                          inp["window"], cu)
+    fq, fk = d_rounding_floor(inp, to_np(o), lse_ref, unit=2.0 ** -12)
     for name, g, r, fl in zip(("dQ", "dK", "dV"), grads, ref, (fq, fk, None)):
         check_grad(to_np(g), r, f"{what} {name}", fl)
 
