@@ -224,9 +224,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, __bf16* lds_base,
-                                      uint32_t voffset) {
+                                      uint32_t voffset, uint32_t soffset = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds_base, 16, (int)voffset,
-                                           0, 0, 0);
+                                           (int)soffset, 0, 0);
 }
 
 // Per-lane byte offsets for staging a [ROWS x D] bf16 tile whose rows are

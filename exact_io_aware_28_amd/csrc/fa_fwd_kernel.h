@@ -85,6 +85,13 @@ void fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) __bf16 v0[kBN * D];
   __shared__ __attribute__((aligned(1024))) __bf16 k1[kBN * D];
   __shared__ __attribute__((aligned(1024))) __bf16 v1[kBN * D];
+  // d = 128 with a bias: each wave's 32 bias rows x 64 keys (fp32) of the
+  // next tile are copied into LDS while the current tile is computed; the
+  // 16-byte chunks of row r sit at positions chunk ^ (r & 15), so the reads
+  // below are free of bank conflicts.  (With both a causal and a window mask
+  // the staging spills registers; that kernel loads the bias directly.)
+  constexpr bool kBiasLds = BIAS && D == 128 && !(CAUSAL && WINDOW);
+  __shared__ __attribute__((aligned(1024))) float bias_s[kBiasLds ? kWaves * 32 * kBN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, r32 = lane & 31;
@@ -145,7 +152,29 @@ void fwd_bf16_kernel(FwdParams p) {
     dma.issue(Kg, kstride_b, j0, sp.lk, kb);
     dma.issue(Vg, kstride_b, j0, sp.lk, vb);
   };
-  if (kv_lo < kv_hi) issue(kv_lo, k0, v0);
+  // bias rows of this wave from key j0 on into its LDS block: eight 1 KB
+  // copies of four rows each.  Copy i, lane l: row 4i + l/16, stored chunk
+  // l % 16, read from chunk (l % 16) ^ (row & 15) = bchunk ^ 4(i % 4); the
+  // row step of 4i rows is a uniform offset.
+  const float* bias_bh = BIAS ? p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh
+                              : nullptr;
+  const int qlo_b = q_start + wave * 32;
+  const uint32_t brow_off = (uint32_t)((lane >> 4) * p.bias_sq) * 4u;
+  const uint32_t bchunk = (uint32_t)((lane & 15) ^ (lane >> 4));
+  auto bias_issue = [&](int j0) __attribute__((always_inline)) {
+    if constexpr (kBiasLds) {
+      const __amdgpu_buffer_rsrc_t rs = bias_rsrc(bias_bh, p.bias_sq, qlo_b, sp.lq, j0, sp.lk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma16(rs, reinterpret_cast<__bf16*>(bias_s + wave * 32 * kBN) + i * 512,
+              brow_off + ((bchunk ^ (uint32_t)(4 * (i & 3))) << 4),
+              (uint32_t)(4 * i * p.bias_sq) * 4u);
+    }
+  };
+  if (kv_lo < kv_hi) {
+    issue(kv_lo, k0, v0);
+    bias_issue(kv_lo);
+  }
   FA_STAGE_SYNC();
 
   // ---- Q fragments (B operand of S^T = K Q^T): query qi, 8 columns per step
@@ -212,7 +241,19 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr int kBiasRegs = BIAS ? NB * 16 : 1;
   const uint32_t bias_lane = (uint32_t)(r32 * p.bias_sq) * 4u;
   auto load_bias = [&](int j0, float (&bt)[kBiasRegs]) {
-    if constexpr (BIAS) {
+    if constexpr (kBiasLds) {
+      // from the LDS block filled during the previous tile
+      const float* brow = bias_s + wave * 32 * kBN + r32 * kBN;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int pos = (kb * 8 + g * 2 + hl) ^ (r32 & 15);
+          const f32x4 t = *reinterpret_cast<const f32x4*>(brow + 4 * pos);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bt[kb * 16 + 4 * g + e] = t[e];
+        }
+    } else if constexpr (BIAS) {
       const __amdgpu_buffer_rsrc_t rs =
           bias_rsrc(p.bias + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh, p.bias_sq, qlo_w,
                     sp.lq, j0, sp.lk);
@@ -231,7 +272,14 @@ void fwd_bf16_kernel(FwdParams p) {
     bool active = qlo_w <= qhi_w;
     if (CAUSAL) active = active && (j0 <= qhi_w + delta);
     if (WINDOW) active = active && (j0 + kBN - 1 > qlo_w + delta - p.window);
-    if (!active) return;
+    if (!active) {
+      // a wave that skips this tile still stages the next tile's bias
+      if constexpr (kBiasLds) {
+        if (j0 + kBN < kv_hi) bias_issue(j0 + kBN);
+        FA_STAGE_SYNC();
+      }
+      return;
+    }
     bool need_mask = (j0 + kBN > sp.lk);
     if (CAUSAL) need_mask = need_mask || (j0 + kBN - 1 > qlo_w + delta);
     if (WINDOW) need_mask = need_mask || (qhi_w + delta - j0 >= p.window);
@@ -274,6 +322,12 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(bt[kb * 16 + i], kLog2e, s[kb][i] * c);
+    }
+    if constexpr (kBiasLds) {
+      // this tile's bias is consumed: copy the next tile's into the block
+      __builtin_amdgcn_sched_barrier(0);
+      if (j0 + kBN < kv_hi) bias_issue(j0 + kBN);
+      FA_STAGE_SYNC();
     }
 
     // A tile that straddles a mask boundary first replaces each invisible
