@@ -370,7 +370,7 @@ def main(argv=None):
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {a.gpus}); "
+        print(f"bench.py: the benchmark runs on exactly one GPU (asked for --gpus {a.gpus}); "
               "the attention path shards over (sequence, KV-head) units with no "
               "communication, so a multi-GPU run is one independent run per GPU.",
               file=sys.stderr)
