@@ -91,6 +91,8 @@ CASES = [
     (1, 190, 190, 8, 1, 128, False, 0, (1, 1, "Q", "K"), 3),       # MQA, strided view
     (1, 130, 130, 2, 2, 64, False, 0, (1, 1, "Q", "K"), 2),        # strided, 16-byte rows
     (1, 64, 64, 2, 1, 128, True, 0, (1, 1, "Q", "K"), 0),          # exact tile
+    (1, 333, 333, 4, 2, 128, False, 70, ("B", "H", "Q", "K"), 0),  # window only: waves skip
+                                                                    # tiles before their window
 ]
 
 

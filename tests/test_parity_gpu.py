@@ -141,6 +141,31 @@ def test_fwd_f16_packed():
     assert np.abs(to_np(dev["o"]) - o_ref).max() < 3e-3
 
 
+# Short causal grids dispatch each XCD's longest query tiles first across the
+# KV-head groups it owns (the launcher's xcd_groups); the condition below
+# restates the launcher's so that each case is known to take that path.
+def _xcd_groups(B, Nq, Hq, Hkv, d):
+    rows = 256 if d == 128 else 128
+    nq = -(-Nq // rows)
+    n, unit = B * Hq * nq, (Hq // Hkv) * nq
+    per, slots = n // 8, 32 * (1 if d == 128 else 3)
+    ok = n % 8 == 0 and per % unit == 0 and per // unit > 1 and per <= 2 * slots
+    return per // unit if ok else 0
+
+
+@pytest.mark.parametrize("case", [
+    (2, 512, 512, 8, 8, 128, True, 0),
+    (4, 600, 600, 8, 4, 128, True, 0),
+    (4, 300, 300, 4, 4, 64, True, 100),
+    (8, 700, 700, 8, 2, 64, True, 0),
+], ids=lambda c: "-".join(map(str, c)))
+def test_fwd_xcd_longest_first(case):
+    B, Nq, Nk, Hq, Hkv, d, causal, window = case
+    assert _xcd_groups(B, Nq, Hq, Hkv, d) > 1, case
+    _compare_full(_dense(B, Nq, Nk, Hq, Hkv, d, causal, window, seed=114),
+                  "xcd order " + str(case))
+
+
 # ------------------------------------------------------------ properties
 def test_scale_zero_gives_counts():
     """scale = 0: LSE = ln(#visible keys) and O = mean of the visible V."""
