@@ -19,7 +19,6 @@
 // Tiles of 32 keys go from HBM into LDS with buffer loads that write LDS
 // directly, two buffers per wave; the products use the same transposed
 // MFMA formulation, LDS swizzle and key permutation as the prefill kernel.
-#include <type_traits>
 
 #include "fa_device.h"
 
@@ -119,7 +118,18 @@ void decode_split_kernel(DecodeParams p) {
     for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
   float m_run = -kInf;  // reference maximum, log2 units
   float l_run = 0.f;    // this half-wave's share of the normaliser
-  const float c = p.scale_log2;
+  // The loop takes the row maximum with a positive multiplier: a negative
+  // scale is applied as |scale| to -Q (sign bits flipped, exact), a zero
+  // scale as a tiny positive one (every exp2(s c - m) still rounds to 1).
+  float c = p.scale_log2;
+  if (c < 0.f) {
+    c = -c;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      qf[st] = as_bf16x8(__builtin_bit_cast(uint4, qf[st]) ^
+                         make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u));
+  }
+  if (c == 0.f) c = 1e-30f;
 
   auto compute = [&](int j0, const __bf16* kt, const __bf16* vt) {
     // S^T: element e holds key j0 + 8(e/4) + 4hl + e%4 for this lane's row
@@ -150,17 +160,11 @@ void decode_split_kernel(DecodeParams p) {
       }
       ce = 1.f;
     }
-    // row extreme in log2 units (max of s*ce: min of s when ce < 0)
+    // row maximum in log2 units (ce is positive)
     float rm = s[0];
-    if (ce >= 0.f) {
 #pragma unroll
-      for (int e = 1; e < 16; ++e) rm = fmaxf(rm, s[e]);
-      rm = fmaxf(rm, xor32(rm));
-    } else {
-#pragma unroll
-      for (int e = 1; e < 16; ++e) rm = fminf(rm, s[e]);
-      rm = fminf(rm, xor32(rm));
-    }
+    for (int e = 1; e < 16; ++e) rm = fmaxf(rm, s[e]);
+    rm = max_halves(rm);
     const float tmax = __builtin_isinf(rm) ? -kInf : rm * ce;
     float m_use = m_run;
     if (tmax > m_run + kRescaleSlack) m_use = tmax;  // also when m_run = -inf
@@ -217,7 +221,7 @@ void decode_split_kernel(DecodeParams p) {
   }
 
   // normalised partial output and its logsumexp (an empty range: 0, -inf)
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   if (!row_ok) return;
   const float inv = (l_tot == 0.f) ? 0.f : 1.0f / l_tot;
   float* op = p.opart + ((((int64_t)split * p.B + b) * Nq + i) * p.Hq + h) * D;

@@ -92,9 +92,6 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }
 
-// Value of lane (l ^ 32): the other half of the wave.
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
 // max(x, x of lane l ^ 32) and x + (x of lane l ^ 32) in every lane, with one
 // v_permlane32_swap (a vector ALU exchange of the two half-waves) instead of
 // the LDS crossbar that a general shuffle uses.

@@ -31,7 +31,6 @@
 // lazily (only when a row maximum grows by more than 1.5 in log2 units): P
 // then stays within E4M3's range with 2^7 of headroom, so probabilities down
 // to 2^-13 of the maximum remain normal numbers.
-#include <type_traits>
 
 #include "fa_device.h"
 

@@ -52,8 +52,6 @@
 //     are unchanged because l and acc always use the same reference.
 #pragma once
 
-#include <type_traits>
-
 #include "fa_device.h"
 
 namespace fa {
