@@ -90,19 +90,22 @@ def test_fp16_bias_dropout_same_bits():
     import exact_io_aware_28_amd as fa
     inp = workloads.make_inputs(dict(B=1, N=300, Hq=4, Hkv=2, d=128, causal=True, seed=904,
                                      bwd=True))
-    say("[debug-sync] fp16 forward, bias forward+backward, dropout forward+backward")
+    say("[debug-sync] fp16 forward+backward, bias forward+backward (causal; window only),"
+        " dropout forward+backward")
     q, k, v, do = (_dev(inp[n]) for n in ("q", "k", "v", "do"))
-    qh, kh, vh = (_dev(inp[n], "f16") for n in ("q", "k", "v"))
+    qh, kh, vh, doh = (_dev(inp[n], "f16") for n in ("q", "k", "v", "do"))
     bias = torch.from_numpy(np.random.default_rng(905).standard_normal((300, 300)).astype(
         np.float32)).cuda()
 
     def run():
         out = fa.fa_fwd_f16(qh, kh, vh, causal=True)
+        gh = fa.fa_bwd_f16(qh, kh, vh, out[0], doh, out[1], causal=True)
         ob, lb = fa.fa_fwd_bias(q, k, v, bias, causal=True)
         gb = fa.fa_bwd_bias(q, k, v, bias, ob, do, lb, causal=True)
+        ow, lw = fa.fa_fwd_bias(q, k, v, bias, window=70)
         od, ld = fa.fa_fwd_dropout(q, k, v, 0.2, 77, causal=True)
         gd = fa.fa_bwd_dropout(q, k, v, od, do, ld, 0.2, 77, causal=True)
-        return out + (ob, lb) + tuple(gb) + (od, ld) + tuple(gd)
+        return (out + tuple(gh) + (ob, lb) + tuple(gb) + (ow, lw) + (od, ld) + tuple(gd))
     _both(run)
 
 
