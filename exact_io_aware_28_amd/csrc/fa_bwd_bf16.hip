@@ -736,13 +736,13 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 }
 
 // ------------------------------------------------------------ 3. dQ
-// Two waves per SIMD; the unmasked d = 128 instances (with or without a
-// bias) do not fit their 256 registers without spilling and run one wave per
-// SIMD instead.  (The masked biased ones fit since the bias entries are kept
-// raw until use: 2.84 vs 3.32 ms for a causal GQA backward with a shared
-// [8192, 8192] bias.)
+// Two waves per SIMD; the unmasked biased d = 128 instance does not fit its
+// 256 registers without spilling and runs one wave per SIMD instead, with the
+// registers that frees spent on loading each half's bias a half ahead.  (The
+// masked biased ones fit since the bias entries are kept raw until use: 2.84
+// vs 3.32 ms for a causal GQA backward with a shared [8192, 8192] bias.)
 template <int D, bool CAUSAL, bool WINDOW, bool BIAS>
-constexpr int dq_waves_per_simd() { return (D == 128 && !CAUSAL && !WINDOW) ? 1 : 2; }
+constexpr int dq_waves_per_simd() { return (D == 128 && !CAUSAL && !WINDOW && BIAS) ? 1 : 2; }
 
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP, bool F16>
 __global__ __launch_bounds__(kThreads)

@@ -238,6 +238,7 @@ BWD_CASES = [
     (1, 100, 300, 4, 2, 128, True, 0),
     (1, 257, 257, 8, 1, 64, True, 0),
     (1, 128, 128, 2, 2, 128, False, 0),
+    (1, 300, 333, 4, 2, 128, False, 0),
 ]
 
 
