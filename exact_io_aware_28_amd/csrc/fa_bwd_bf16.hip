@@ -566,6 +566,17 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
         const int qr = qr0 + 8 * (i >> 2) + 4 * hl + (i & 3);
         bv[i] = (kj < sp.lk && qr < sp.lq) ? bcol[(int64_t)qr * p.bias_sq] : 0.f;
       }
+      // An element the mask hides gets the bias -inf: its probability
+      // exp2(... - inf) is exactly zero, so dS is too, whatever the scale,
+      // and one update serves every tile (a second, masked copy of it
+      // spilled registers in the masked biased kernels).
+      if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qr = qr0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (!visible<CAUSAL, WINDOW>(qr, kj, delta, sp.lk, p.window)) bv[i] = -kInf;
+        }
+      }
     }
 
     // S = Q K^T and dP = dO V^T: lane = key kj, rows = queries
@@ -630,7 +641,7 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
         }
       }
     };
-    if (need_mask)
+    if (!BIAS && need_mask)
       grads(std::true_type{});
     else
       grads(std::false_type{});
@@ -882,12 +893,12 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
     // qi, rows = keys j0 + 32kb + 8(i/4) + 4hl + i%4.
     // Without a bias the half computes P for every element and zeroes the
     // invisible entries of a masked half in a separate, rarely taken step
-    // before one dS update (long causal backward 1.6 % faster); the biased
-    // kernels keep the masking inline in two copies of the half (the split
-    // form spills there).
+    // before one dS update (long causal backward 1.6 % faster); with a bias
+    // an invisible element's bias becomes -inf in such a step instead, so
+    // its probability is exactly zero (the split form spills there).  Either
+    // way one dS update serves masked and unmasked halves.
     constexpr bool kSplitMask = !BIAS;
-    auto half = [&](int kb, auto masked_tag) __attribute__((always_inline)) {
-      constexpr bool MASKED = !kSplitMask && decltype(masked_tag)::value;
+    auto half = [&](int kb) __attribute__((always_inline)) {
       float bv[BIAS ? 16 : 1];
       if constexpr (kBiasAhead) {
 #pragma unroll
@@ -897,6 +908,23 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
         if (nj < kv_hi) load_bias_half(nj, (kb + 1 < NB) ? kb + 1 : 0, bnext);
       } else if constexpr (BIAS) {
         load_bias_half(j0, kb, bv);
+      }
+      // this lane's key of element i is j0 + 32kb + 4hl + 8(i/4) + i%4
+      const int base = j0 + kb * 32 + 4 * hl;
+      const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
+      auto visible_off = [&](int i) {
+        const int off = (i >> 2) * 8 + (i & 3);
+        bool ok = off < end;
+        if (CAUSAL) ok = ok && off <= hi;
+        if (WINDOW) ok = ok && off > lo;
+        return ok;
+      };
+      if constexpr (BIAS) {
+        if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (!visible_off(i)) bv[i] = -kInf;
+        }
       }
       f32x16 s, dp;
 #pragma unroll
@@ -918,8 +946,6 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 
       // P = exp2(S c - LSE log2 e), dS = P (dP - D); element i holds key
       // base + off with off = 8(i/4) + i%4
-      const int base = j0 + kb * 32 + 4 * hl;
-      const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
       // dropout: two generator calls cover the half's 16 keys of this lane,
       // base + 16c + 8a + {0..3}: element i takes slot i & 7 of call i >> 3
       uint4 dw[2];
@@ -928,13 +954,6 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
         for (int c2 = 0; c2 < 2; ++c2)
           dw[c2] = drop_call(base + 16 * c2, qi, h, b, p.seed_lo, p.seed_hi);
       }
-      auto visible_off = [&](int i) {
-        const int off = (i >> 2) * 8 + (i & 3);
-        bool ok = off < end;
-        if (CAUSAL) ok = ok && off <= hi;
-        if (WINDOW) ok = ok && off > lo;
-        return ok;
-      };
       auto ds_of = [&](int i, float pv) {
         if constexpr (DROP)
           dp[i] = pv * ((slot_of(dw[i >> 3], i & 7) >= p.drop_thresh ? dp[i] * p.drop_scale
@@ -959,9 +978,7 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
         for (int i = 0; i < 16; ++i) {
           float pv = fmaf(s[i], c, -lse2);
           if constexpr (BIAS) pv = fmaf(bv[i], kLog2e, pv);
-          pv = fast_exp2(pv);
-          if (MASKED) pv = visible_off(i) ? pv : 0.f;
-          ds_of(i, pv);
+          ds_of(i, fast_exp2(pv));
         }
       }
 
@@ -982,12 +999,7 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       }
     };
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      if (!kSplitMask && need_mask)
-        half(kb, std::true_type{});
-      else
-        half(kb, std::false_type{});
-    }
+    for (int kb = 0; kb < NB; ++kb) half(kb);
   };
 
 #pragma nounroll
