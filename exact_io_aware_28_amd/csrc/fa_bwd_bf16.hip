@@ -475,7 +475,11 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
   auto it_tile = [&](int it) { return BIAS ? it / G : it % n_qt; };
 
   const int64_t qstride = (int64_t)p.Hq * D, kstride = (int64_t)p.Hkv * D;
-  const float c = p.scale_log2;
+  // With dropout a hidden score is replaced by a value whose product with c
+  // is -inf: -inf for a positive c, +inf for a negative one; a zero c is
+  // taken as 1e-30, which leaves exp2(S c - L) as it was for a finite score.
+  const float c = (DROP && p.scale_log2 == 0.f) ? 1e-30f : p.scale_log2;
+  const float s_hidden = (c > 0.f) ? -kInf : kInf;
 
   const int kw_lo = k_start + kw * 32;
   const int kw_hi = min(kw_lo + 31, sp.lk - 1);
@@ -592,6 +596,22 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
                   as_bf16x8(lds_read_b128_at(sv, fk[st], 0)), dp);
     }
 
+    // With dropout a tile that a mask crosses first replaces each hidden
+    // score by s_hidden (a rarely taken step), so that its probability is
+    // exactly zero and one update serves every tile: a second, masked copy
+    // of the update next to the keep bits spilled 176 bytes per lane.  (A
+    // bias carries the mask itself; without either, two copies measured
+    // faster.)
+    if constexpr (DROP) {
+      if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qr = qr0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (!visible<CAUSAL, WINDOW>(qr, kj, delta, sp.lk, p.window)) s[i] = s_hidden;
+        }
+      }
+    }
+
     // dropout keep bits, drawn and shared as in the one-wave-per-SIMD kernel
     uint32_t kwd[8];
     if constexpr (DROP) {
@@ -641,7 +661,7 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
         }
       }
     };
-    if (!BIAS && need_mask)
+    if (!BIAS && !DROP && need_mask)
       grads(std::true_type{});
     else
       grads(std::false_type{});
@@ -1031,11 +1051,12 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
 }
 
 // dK/dV kernel choice: the eight-wave kernel for d = 128 without dropout.
-// d = 64 already runs two waves per SIMD in the four-wave kernel; with
-// dropout the eight-wave kernel spills 40-60 registers (the keep-bit words)
-// and measured 3.36 vs 2.61 ms on the dropout workload.
+// d = 64 already runs two waves per SIMD in the four-wave kernel.  With
+// dropout the eight-wave kernel (one update body) is faster than the
+// four-wave one at one wave per SIMD: 2.201 vs 2.390 ms for the backward of
+// the GQA prefill shape with p = 0.1.
 template <int D, bool DROP>
-constexpr bool kUseDkdv8 = D == 128 && !DROP;
+constexpr bool kUseDkdv8 = D == 128;
 
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false, bool DROP = false,
           bool F16 = false>
