@@ -163,3 +163,12 @@ def test_bias_workload_sampled():
     check_grad(dq[0][qr][:, 4 * g:4 * g + 4], rq, "gqa_bias dQ")
     check_grad(dk[0, kr, g], rk, "gqa_bias dK")
     check_grad(dv[0, kr, g], rv, "gqa_bias dV")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_bias_scale_sign(scale):
+    """A negative and a zero scale with a bias and a causal mask: the masked
+    elements of the backward get a -inf bias, whatever the scale's sign."""
+    inp = _inputs(1, 300, 300, 4, 2, 128, True, 0, (1, 1, "Q", "K"), seed=240)
+    inp["scale"] = scale
+    _check_full(inp, f"bias, causal, scale={scale}")

@@ -310,3 +310,25 @@ def test_dropout_gqa_prefill_sampled():
     check_grad(dq[0][qr][:, 4 * g:4 * g + 4], rq, "dropout dQ")
     check_grad(dk[0, kr, g], rk, "dropout dK")
     check_grad(dv[0, kr, g], rv, "dropout dV")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_dropout_scale_sign(scale):
+    """Dropout with a negative and with a zero scale, causal over several
+    tiles: the dK/dV kernel hides masked scores with a sentinel chosen by the
+    scale's sign (a zero scale is taken as a tiny positive one)."""
+    inp = workloads.make_inputs(dict(B=1, Nq=300, Nk=300, Hq=4, Hkv=2, d=128, causal=True,
+                                     window=0, seed=350, bwd=True, scale=scale))
+    pf, seed = _f32(0.2), 4242
+    what = f"dropout causal scale={scale}"
+    say(f"[dropout] {what}")
+    o, lse, grads = _run(inp, pf, seed)
+    f = lambda n: inp[n].astype(np.float64)
+    o_ref, lse_ref = oracle.attn_fwd(f("q"), f("k"), f("v"), scale, True, 0, dropout_p=pf,
+                                     seed=seed)
+    check_o(to_np(o), o_ref, what, dropout_bar_scale(pf))
+    check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, what)
+    ref = oracle.attn_bwd(f("q"), f("k"), f("v"), f("do"), scale, True, 0, dropout_p=pf,
+                          seed=seed)
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+        check_grad(to_np(g), r, f"{what} {name}")

@@ -416,3 +416,18 @@ def test_workload_long_bwd_whole_head():
     check_grad(dq, rq, "dQ whole head")
     check_grad(dk, rk, "dK whole head")
     check_grad(dv, rv, "dV whole head")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_bwd_scale_sign(scale):
+    """The backward with a negative and with a zero scale (several query and
+    key tiles, causal, so diagonal tiles are masked).  With scale 0 the exact
+    dQ and dK vanish, and the bar asks for exact zeros."""
+    inp = _dense(1, 300, 300, 4, 2, 128, True, 0, seed=121, bwd=True, scale=scale)
+    say(f"[bwd] scale={scale}")
+    dev = run_fwd(inp)
+    dq, dk, dv = run_bwd(inp, dev)
+    rq, rk, rv = _oracle_bwd(inp)
+    check_grad(to_np(dq), rq, f"scale={scale} dQ")
+    check_grad(to_np(dk), rk, f"scale={scale} dK")
+    check_grad(to_np(dv), rv, f"scale={scale} dV")
