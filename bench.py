@@ -5,6 +5,7 @@
     python bench.py --backward [--workload long_fwd_bwd] [--dtype bf16|f16] [--steps K]
                     [--warmup W]
     python bench.py --decode [--steps K] [--warmup W]
+    python bench.py --fp8 [--steps K] [--warmup W]
 
 One step = one fa_fwd call over the whole workload: work partition, Q/K/V
 tile loads, QK^T, masking, online softmax, PV and the epilogue all run in the
@@ -20,7 +21,9 @@ With --backward it times only the backward call (D, dK/dV and dQ kernels) of
 a workload that has one and prints one line with its time and throughput on
 the five counted products (2.5x the forward count); this is the mode the
 backward's kernel traces and counters are taken from.  --decode does the
-same for the split-KV decode workload (split and combine kernels).
+same for the split-KV decode workload (split and combine kernels), --fp8 for
+the FP8 forward of the GQA prefill shape and the quantizer that makes its
+inputs.
 """
 
 import argparse
@@ -367,6 +370,9 @@ def main(argv=None):
                     help="with --backward: operand type (default: the workload's, bf16)")
     ap.add_argument("--decode", action="store_true",
                     help="time only the split-KV decode workload")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time only the FP8 forward of the GQA prefill shape and its "
+                         "quantizer")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -390,6 +396,10 @@ def main(argv=None):
     if a.decode:
         for name in workloads.DECODE_WORKLOADS:
             print(json.dumps(decode_line(name, a.steps, a.warmup)), flush=True)
+        return 0
+
+    if a.fp8:
+        print(json.dumps(time_fp8("gqa_causal_prefill_fp8", a.steps, a.warmup)), flush=True)
         return 0
 
     if a.backward:
