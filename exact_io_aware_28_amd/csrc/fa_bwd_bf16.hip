@@ -19,7 +19,7 @@
 //      key); it walks every query head of the KV head's group and every
 //      query tile that can see its keys, with Q, dO, LSE and D tiles staged
 //      in LDS.  dK and dV stay in registers and are written once, so the GQA
-//      sum over the group needs no atomics.  For d = 128 (no dropout) eight
+//      sum over the group needs no atomics.  For d = 128 eight
 //      waves share the work, K and V staged in LDS, each pair of waves
 //      splitting every query tile's rows and adding its partial sums at the
 //      end (bwd_dkdv8_kernel); otherwise four waves, one per 32 keys, with K
@@ -612,7 +612,7 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
       }
     }
 
-    // dropout keep bits, drawn and shared as in the one-wave-per-SIMD kernel
+    // dropout keep bits, drawn and shared as in the four-wave kernel
     uint32_t kwd[8];
     if constexpr (DROP) {
       const int t = r32 & 3, a = (r32 >> 3) & 1, u = 4 * a + t;
@@ -1050,12 +1050,12 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   }
 }
 
-// dK/dV kernel choice: the eight-wave kernel for d = 128 without dropout.
-// d = 64 already runs two waves per SIMD in the four-wave kernel.  With
-// dropout the eight-wave kernel (one update body) is faster than the
-// four-wave one at one wave per SIMD: 2.201 vs 2.390 ms for the backward of
-// the GQA prefill shape with p = 0.1.
-template <int D, bool DROP>
+// dK/dV kernel choice: the eight-wave kernel for d = 128, the four-wave one
+// for d = 64 (which already runs two waves per SIMD there).  With dropout too
+// the eight-wave kernel (one update body) is faster than the four-wave one at
+// one wave per SIMD: 2.201 vs 2.390 ms for the backward of the GQA prefill
+// shape with p = 0.1.
+template <int D>
 constexpr bool kUseDkdv8 = D == 128;
 
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false, bool DROP = false,
@@ -1063,7 +1063,7 @@ template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS = false, bool 
 hipError_t launch4(const BwdParams& p, hipStream_t stream) {
   const int nkt = (p.Nk + kKeyBlock - 1) / kKeyBlock;
   const int nqt = (p.Nq + kQBlock - 1) / kQBlock;
-  if constexpr (kUseDkdv8<D, DROP>)
+  if constexpr (kUseDkdv8<D>)
     hipLaunchKernelGGL((bwd_dkdv8_kernel<D, CAUSAL, WINDOW, VARLEN, BIAS, DROP, F16>),
                        dim3((unsigned)p.B * p.Hkv * nkt), dim3(kDkdv8Threads), 0, stream, p, nkt);
   else
