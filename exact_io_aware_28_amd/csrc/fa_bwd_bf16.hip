@@ -767,17 +767,14 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
 }
 
 // ------------------------------------------------------------ 3. dQ
-// Two waves per SIMD; the unmasked biased d = 128 instance does not fit its
-// 256 registers without spilling and runs one wave per SIMD instead, with the
-// registers that frees spent on loading each half's bias a half ahead.  (The
-// masked biased ones fit since the bias entries are kept raw until use: 2.84
-// vs 3.32 ms for a causal GQA backward with a shared [8192, 8192] bias.)
-template <int D, bool CAUSAL, bool WINDOW, bool BIAS>
-constexpr int dq_waves_per_simd() { return (D == 128 && !CAUSAL && !WINDOW && BIAS) ? 1 : 2; }
-
+// Two waves per SIMD in every instance.  With one dS update for masked and
+// unmasked halves even the biased d = 128 kernels fit 256 registers; the
+// unmasked one had run one wave per SIMD with each half's bias loaded a half
+// ahead, and runs the biased GQA backward in 4.867 vs 5.513 ms at two.  (The
+// bias entries are kept raw until use: 2.84 vs 3.32 ms for a causal GQA
+// backward with a shared [8192, 8192] bias.)
 template <int D, bool CAUSAL, bool WINDOW, bool VARLEN, bool BIAS, bool DROP, bool F16>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<D, CAUSAL, WINDOW, BIAS>())))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(BwdParams p, int num_qtiles) {
   constexpr int KS = D / 16, DB = D / 32, NB = kKTile / 32, NC = kKTile / 16;
   constexpr float kInf = __builtin_inff();
@@ -861,16 +858,6 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
       for (int e = 0; e < 4; ++e) dst[4 * g + e] = t[e];
     }
   };
-  // At one wave per SIMD (d = 128 without a causal or window mask) there
-  // are registers to spare: each half loads the next half's bias into
-  // bnext, a whole half ahead of its use, instead of its own just before the
-  // products (2.38 vs 2.82 ms for the dQ kernel of a GQA backward with a
-  // shared [8192, 8192] bias; a whole tile ahead measured 2.43 ms).
-  constexpr bool kBiasAhead = BIAS && dq_waves_per_simd<D, CAUSAL, WINDOW, BIAS>() == 1;
-  float bnext[kBiasAhead ? 16 : 1];
-  if constexpr (kBiasAhead) {
-    if (kv_lo < kv_hi) load_bias_half(kv_lo, 0, bnext);
-  }
 
   // Lane byte offsets of the LDS reads inside a K or V tile (same swizzled
   // layout as the forward): 128-bit fragment reads per k-step, transposing
@@ -920,15 +907,7 @@ void bwd_dq_kernel(BwdParams p, int num_qtiles) {
     constexpr bool kSplitMask = !BIAS;
     auto half = [&](int kb) __attribute__((always_inline)) {
       float bv[BIAS ? 16 : 1];
-      if constexpr (kBiasAhead) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bv[i] = bnext[i];
-        // the next half: this tile's second, or the next tile's first
-        const int nj = (kb + 1 < NB) ? j0 : j0 + kKTile;
-        if (nj < kv_hi) load_bias_half(nj, (kb + 1 < NB) ? kb + 1 : 0, bnext);
-      } else if constexpr (BIAS) {
-        load_bias_half(j0, kb, bv);
-      }
+      if constexpr (BIAS) load_bias_half(j0, kb, bv);
       // this lane's key of element i is j0 + 32kb + 4hl + 8(i/4) + i%4
       const int base = j0 + kb * 32 + 4 * hl;
       const int end = sp.lk - base, hi = qi + delta - base, lo = qi + delta - p.window - base;
