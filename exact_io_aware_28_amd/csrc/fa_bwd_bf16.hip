@@ -545,6 +545,11 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
     }
   };
 
+  // Bias at this lane's key for its 16 query rows of the current tile (raw
+  // values, scaled to log2 units where they are used).  A bias shared by the
+  // heads (head stride 0) is loaded once per query tile and serves the tile's
+  // G iterations (heads innermost): biased GQA backward 4.33 vs 4.83 ms.
+  float bv[BIAS ? 16 : 1];
   auto compute = [&](int it, const __bf16* tq, const __bf16* tdo, const float* tl,
                      const float* td) {
     const int i0 = q_lo + it_tile(it) * kQTile;
@@ -559,10 +564,10 @@ void bwd_dkdv8_kernel(BwdParams p, int num_ktiles) {
     if (CAUSAL) need_mask = need_mask || (qr0 + delta < kw_hi);
     if (WINDOW) need_mask = need_mask || (qr1 + delta - kw_lo >= p.window);
 
-    // bias at this lane's key for the block's 16 query rows (raw values,
-    // scaled to log2 units where they are used)
-    float bv[BIAS ? 16 : 1];
-    if constexpr (BIAS) {
+    // a new query tile, or a bias of its own per head: load it (a wave
+    // that skips a tile skips all of its heads, so bv always holds this
+    // tile's bias when it is used; the mask depends on the tile only)
+    if (BIAS && (p.bias_sh != 0 || it_head(it) == 0)) {
       const float* bcol = p.bias + (int64_t)b * p.bias_sb + (int64_t)h_it * p.bias_sh +
                           min(kj, sp.lk - 1);
 #pragma unroll
